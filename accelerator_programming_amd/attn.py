@@ -1,0 +1,207 @@
+"""ctypes binding of the C ABI in include/attn_fwd.h (argument marshalling only).
+
+The names mirror the C entry points: ``attn_fwd_create``,
+``attn_fwd_create_ex``, ``attn_fwd_run``, ``attn_fwd_destroy``,
+``attn_status_str`` and ``attn_fwd_plan_info``. Every step of the attention
+pass runs inside the HIP library; torch only provides device memory and the
+stream. If the library has not been built this module raises on first use:
+there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn_fwd.so")
+
+ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP, ATTN_ERR_NOMEM = range(5)
+ATTN_BF16, ATTN_FP32 = 0, 1
+
+_I64x3 = ctypes.c_int64 * 3
+
+
+class AttnFwdParams(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int64), ("H_q", ctypes.c_int64), ("H_kv", ctypes.c_int64),
+        ("N", ctypes.c_int64), ("d", ctypes.c_int64), ("N_kv", ctypes.c_int64),
+        ("d_v", ctypes.c_int64), ("causal", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("dtype", ctypes.c_int32),
+        ("q_strides", _I64x3), ("k_strides", _I64x3), ("v_strides", _I64x3),
+        ("o_strides", _I64x3),
+    ]
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s failed: %s" % (where, attn_status_str(status)))
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("HIP library %s is not built; run "
+                               "`python -m accelerator_programming_amd.build`" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        L.attn_fwd_create.restype = ctypes.c_int
+        L.attn_fwd_create.argtypes = [ctypes.POINTER(P), I64, I64, I64, I64, I64, ctypes.c_int32,
+                                      ctypes.c_float]
+        L.attn_fwd_create_ex.restype = ctypes.c_int
+        L.attn_fwd_create_ex.argtypes = [ctypes.POINTER(AttnFwdParams), ctypes.POINTER(P)]
+        L.attn_fwd_run.restype = ctypes.c_int
+        L.attn_fwd_run.argtypes = [P, P, P, P, P, P, P]
+        L.attn_fwd_destroy.restype = None
+        L.attn_fwd_destroy.argtypes = [P]
+        L.attn_status_str.restype = ctypes.c_char_p
+        L.attn_status_str.argtypes = [ctypes.c_int]
+        L.attn_fwd_plan_info.restype = ctypes.c_int
+        L.attn_fwd_plan_info.argtypes = [P, ctypes.POINTER(I64), ctypes.POINTER(ctypes.c_int32),
+                                         ctypes.POINTER(ctypes.c_int32),
+                                         ctypes.POINTER(ctypes.c_int32),
+                                         ctypes.POINTER(ctypes.c_int32)]
+        _lib = L
+    return _lib
+
+
+def attn_status_str(status: int) -> str:
+    return lib().attn_status_str(int(status)).decode()
+
+
+def attn_fwd_create(B: int, H_q: int, H_kv: int, N: int, d: int, causal: bool,
+                    scale: float) -> int:
+    plan = ctypes.c_void_p()
+    st = lib().attn_fwd_create(ctypes.byref(plan), B, H_q, H_kv, N, d, int(bool(causal)),
+                               float(scale))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_create")
+    return plan.value
+
+
+def attn_fwd_create_ex(params: AttnFwdParams) -> int:
+    plan = ctypes.c_void_p()
+    st = lib().attn_fwd_create_ex(ctypes.byref(params), ctypes.byref(plan))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_create_ex")
+    return plan.value
+
+
+def attn_fwd_run(plan: int, Q: int, K: int, V: int, O: int, lse: int | None,
+                 stream: int | None) -> None:
+    """Pointers are integers (e.g. ``tensor.data_ptr()``); stream is a
+    hipStream_t as an integer (``torch.cuda.current_stream().cuda_stream``)."""
+    st = lib().attn_fwd_run(plan, Q, K, V, O, lse or None, stream or None)
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_run")
+
+
+def attn_fwd_destroy(plan: int | None) -> None:
+    lib().attn_fwd_destroy(plan)
+
+
+def attn_fwd_plan_info(plan: int) -> dict:
+    g = ctypes.c_int64()
+    b, tq, tk, lds = (ctypes.c_int32() for _ in range(4))
+    st = lib().attn_fwd_plan_info(plan, ctypes.byref(g), ctypes.byref(b), ctypes.byref(tq),
+                                  ctypes.byref(tk), ctypes.byref(lds))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_plan_info")
+    return {"grid": g.value, "block": b.value, "tile_q": tq.value, "tile_k": tk.value,
+            "lds_bytes": lds.value}
+
+
+# ---------------------------------------------------------------------------
+# torch-facing helpers (shapes and strides only; no arithmetic)
+# ---------------------------------------------------------------------------
+def params_for(q, k, v, causal: bool, scale: float | None = None, o=None) -> AttnFwdParams:
+    """Descriptor for tensors q [B,H_q,N,d], k [B,H_kv,N_kv,d], v [B,H_kv,N_kv,d_v]."""
+    import torch
+    if q.dtype == torch.bfloat16:
+        dt = ATTN_BF16
+    elif q.dtype == torch.float32:
+        dt = ATTN_FP32
+    else:
+        raise TypeError("q must be bfloat16 or float32, got %s" % q.dtype)
+    for name, t in (("k", k), ("v", v)) + ((("o", o),) if o is not None else ()):
+        if t.dtype != q.dtype:
+            raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, q.dtype))
+    for name, t in (("q", q), ("k", k), ("v", v)) + ((("o", o),) if o is not None else ()):
+        if t.dim() != 4:
+            raise ValueError("%s must be 4-D [B, H, N, d]" % name)
+        if t.stride(3) != 1:
+            raise ValueError("%s must have unit stride in its last dimension" % name)
+    B, Hq, N, d = q.shape
+    _, Hkv, Nkv, dk = k.shape
+    dv = v.shape[3]
+    if tuple(k.shape[:1]) != (B,) or dk != d or tuple(v.shape[:3]) != (B, Hkv, Nkv):
+        raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape),
+                                                          tuple(v.shape)))
+    p = AttnFwdParams()
+    p.B, p.H_q, p.H_kv, p.N, p.d, p.N_kv, p.d_v = B, Hq, Hkv, N, d, Nkv, dv
+    p.causal = int(bool(causal))
+    p.scale = float(scale) if scale is not None else 1.0 / math.sqrt(d)
+    p.dtype = dt
+    p.q_strides = _I64x3(*q.stride()[:3])
+    p.k_strides = _I64x3(*k.stride()[:3])
+    p.v_strides = _I64x3(*v.stride()[:3])
+    if o is not None:
+        p.o_strides = _I64x3(*o.stride()[:3])
+    else:
+        p.o_strides = _I64x3(Hq * N * dv, N * dv, dv)
+    return p
+
+
+class AttnFwd:
+    """A plan bound to tensor shapes/strides; ``__call__`` runs it."""
+
+    def __init__(self, q, k, v, causal: bool, scale: float | None = None, o=None):
+        self.params = params_for(q, k, v, causal, scale, o)
+        self.plan = attn_fwd_create_ex(self.params)
+
+    def info(self) -> dict:
+        return attn_fwd_plan_info(self.plan)
+
+    def run(self, q, k, v, o, lse=None, stream=None) -> None:
+        import torch
+        for t in (q, k, v, o) + ((lse,) if lse is not None else ()):
+            if not t.is_cuda:
+                raise ValueError("attn_fwd_run needs device tensors")
+        if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
+            raise ValueError("lse must be a contiguous float32 tensor")
+        s = stream if stream is not None else torch.cuda.current_stream()
+        attn_fwd_run(self.plan, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                     lse.data_ptr() if lse is not None else None, s.cuda_stream)
+
+    __call__ = run
+
+    def close(self) -> None:
+        if self.plan:
+            attn_fwd_destroy(self.plan)
+            self.plan = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def attention(q, k, v, causal: bool = False, scale: float | None = None, with_lse: bool = True):
+    """Allocate O (and lse) with torch and run the HIP kernel once."""
+    import torch
+    B, Hq, N, _ = q.shape
+    o = torch.empty((B, Hq, N, v.shape[3]), dtype=q.dtype, device=q.device)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if with_lse else None
+    op = AttnFwd(q, k, v, causal, scale, o)
+    try:
+        op.run(q, k, v, o, lse)
+    finally:
+        op.close()
+    return o, lse

@@ -1,0 +1,217 @@
+// C ABI of the gfx950 attention forward library: plan creation (host-only
+// validation and variant choice), launch, and teardown. The declarations and
+// their contracts are in include/attn_fwd.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <new>
+
+#include "../../include/attn_fwd.h"
+#include "attn_fwd_kernel.hpp"
+
+using attn::KernelArgs;
+using attn::TileCfg;
+
+namespace {
+
+enum Variant : int32_t {
+    V_D64_BF16 = 0,
+    V_D128_BF16 = 1,
+    V_D64_FP32 = 2,
+};
+
+}  // namespace
+
+struct attn_fwd_plan {
+    attn_fwd_params p;  // strides filled in
+    int32_t variant;
+    int32_t tile_q, tile_k, block, lds_bytes;
+    int64_t n_qtiles, grid;
+    float c;  // scale * log2(e)
+};
+
+namespace {
+
+constexpr int64_t kMaxSlab = (int64_t)1 << 31;
+
+bool fill_strides(int64_t s[3], int64_t H, int64_t N, int64_t d, int64_t row_min,
+                  int64_t align_elems) {
+    if (s[0] == 0 && s[1] == 0 && s[2] == 0) {
+        s[2] = d;
+        s[1] = N * d;
+        s[0] = H * N * d;
+    }
+    for (int i = 0; i < 3; ++i)
+        if (s[i] < 0 || s[i] % align_elems != 0) return false;
+    if (s[2] < row_min) return false;
+    // every element offset inside one [N, d] slab must fit in 31 bits
+    if ((N - 1) * s[2] + d > kMaxSlab) return false;
+    return true;
+}
+
+attn_status validate(const attn_fwd_params *in, attn_fwd_plan *out) {
+    attn_fwd_params p = *in;
+    if (p.N_kv == 0) p.N_kv = p.N;
+    if (p.d_v == 0) p.d_v = p.d;
+    if (p.B < 1 || p.H_q < 1 || p.H_kv < 1 || p.N < 1 || p.d < 1 || p.N_kv < 1 || p.d_v < 1)
+        return ATTN_ERR_INVALID;
+    if (p.H_q % p.H_kv != 0) return ATTN_ERR_INVALID;
+    if (p.causal != 0 && p.causal != 1) return ATTN_ERR_INVALID;
+    if (p.causal && p.N_kv != p.N) return ATTN_ERR_INVALID;
+    if (!std::isfinite(p.scale) || !(p.scale > 0.f)) return ATTN_ERR_INVALID;
+    if (p.dtype != ATTN_BF16 && p.dtype != ATTN_FP32) return ATTN_ERR_INVALID;
+    // grid and index arithmetic run in 32 bits inside the kernel
+    if (p.B * p.H_q > ((int64_t)1 << 30) || p.N > ((int64_t)1 << 30) || p.N_kv > ((int64_t)1 << 30))
+        return ATTN_ERR_UNSUPPORTED;
+
+    const int64_t align = (p.dtype == ATTN_BF16) ? 8 : 4;
+    if (!fill_strides(p.q_strides, p.H_q, p.N, p.d, p.d, align)) return ATTN_ERR_INVALID;
+    if (!fill_strides(p.k_strides, p.H_kv, p.N_kv, p.d, p.d, align)) return ATTN_ERR_INVALID;
+    if (!fill_strides(p.v_strides, p.H_kv, p.N_kv, p.d_v, p.d_v, align)) return ATTN_ERR_INVALID;
+    if (!fill_strides(p.o_strides, p.H_q, p.N, p.d_v, p.d_v, align)) return ATTN_ERR_INVALID;
+
+    int32_t variant;
+    if (p.d == 64 && p.d_v == 64 && p.dtype == ATTN_BF16) variant = V_D64_BF16;
+    else if (p.d == 128 && p.d_v == 128 && p.dtype == ATTN_BF16) variant = V_D128_BF16;
+    else if (p.d == 64 && p.d_v == 64 && p.dtype == ATTN_FP32) variant = V_D64_FP32;
+    else return ATTN_ERR_UNSUPPORTED;
+
+    out->p = p;
+    out->variant = variant;
+    if (variant == V_D128_BF16) {
+        out->tile_q = TileCfg<128>::TQ;
+        out->tile_k = TileCfg<128>::TK;
+        out->block = TileCfg<128>::NT;
+        out->lds_bytes = TileCfg<128>::LDS_BYTES;
+    } else {
+        out->tile_q = TileCfg<64>::TQ;
+        out->tile_k = TileCfg<64>::TK;
+        out->block = TileCfg<64>::NT;
+        out->lds_bytes = TileCfg<64>::LDS_BYTES;
+    }
+    out->n_qtiles = (p.N + out->tile_q - 1) / out->tile_q;
+    out->grid = out->n_qtiles * p.B * p.H_q;
+    if (out->grid > 0x7fffffff) return ATTN_ERR_UNSUPPORTED;
+    out->c = (float)((double)p.scale * 1.4426950408889634074);
+    return ATTN_OK;
+}
+
+template <int D, bool CAUSAL, typename T>
+hipError_t launch(const attn_fwd_plan *pl, const KernelArgs &a, hipStream_t stream) {
+    hipLaunchKernelGGL((attn::attn_fwd_kernel<D, CAUSAL, T>), dim3((uint32_t)pl->grid),
+                       dim3(pl->block), 0, stream, a);
+    return hipGetLastError();
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_fwd_create_ex(const attn_fwd_params *params, attn_fwd_plan **plan) {
+    if (!plan) return ATTN_ERR_INVALID;
+    *plan = nullptr;
+    if (!params) return ATTN_ERR_INVALID;
+    attn_fwd_plan tmp;
+    const attn_status st = validate(params, &tmp);
+    if (st != ATTN_OK) return st;
+    attn_fwd_plan *p = new (std::nothrow) attn_fwd_plan(tmp);
+    if (!p) return ATTN_ERR_NOMEM;
+    *plan = p;
+    return ATTN_OK;
+}
+
+attn_status attn_fwd_create(attn_fwd_plan **plan, int64_t B, int64_t H_q, int64_t H_kv, int64_t N,
+                            int64_t d, int32_t causal, float scale) {
+    attn_fwd_params p = {};
+    p.B = B;
+    p.H_q = H_q;
+    p.H_kv = H_kv;
+    p.N = N;
+    p.d = d;
+    p.causal = causal;
+    p.scale = scale;
+    p.dtype = ATTN_BF16;
+    return attn_fwd_create_ex(&p, plan);
+}
+
+attn_status attn_fwd_run(const attn_fwd_plan *plan, const void *Q, const void *K, const void *V,
+                         void *O, float *lse, void *stream) {
+    if (!plan || !Q || !K || !V || !O) return ATTN_ERR_INVALID;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) ||
+        (lse && ((uintptr_t)lse & 3u)))
+        return ATTN_ERR_INVALID;
+    const attn_fwd_params &p = plan->p;
+    KernelArgs a;
+    a.q = Q;
+    a.k = K;
+    a.v = V;
+    a.o = O;
+    a.lse = lse;
+    a.q_sb = p.q_strides[0];
+    a.q_sh = p.q_strides[1];
+    a.q_sn = (int32_t)p.q_strides[2];
+    a.k_sb = p.k_strides[0];
+    a.k_sh = p.k_strides[1];
+    a.k_sn = (int32_t)p.k_strides[2];
+    a.v_sb = p.v_strides[0];
+    a.v_sh = p.v_strides[1];
+    a.v_sn = (int32_t)p.v_strides[2];
+    a.o_sb = p.o_strides[0];
+    a.o_sh = p.o_strides[1];
+    a.o_sn = (int32_t)p.o_strides[2];
+    a.B = (int32_t)p.B;
+    a.Hq = (int32_t)p.H_q;
+    a.Hkv = (int32_t)p.H_kv;
+    a.Nq = (int32_t)p.N;
+    a.Nkv = (int32_t)p.N_kv;
+    a.group = (int32_t)(p.H_q / p.H_kv);
+    a.n_qtiles = (int32_t)plan->n_qtiles;
+    a.c = plan->c;
+
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    switch (plan->variant) {
+        case V_D64_BF16:
+            e = p.causal ? launch<64, true, __bf16>(plan, a, s) : launch<64, false, __bf16>(plan, a, s);
+            break;
+        case V_D128_BF16:
+            e = p.causal ? launch<128, true, __bf16>(plan, a, s) : launch<128, false, __bf16>(plan, a, s);
+            break;
+        case V_D64_FP32:
+            e = p.causal ? launch<64, true, float>(plan, a, s) : launch<64, false, float>(plan, a, s);
+            break;
+        default:
+            return ATTN_ERR_INVALID;
+    }
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+void attn_fwd_destroy(attn_fwd_plan *plan) { delete plan; }
+
+const char *attn_status_str(attn_status status) {
+    switch (status) {
+        case ATTN_OK: return "ATTN_OK";
+        case ATTN_ERR_INVALID: return "ATTN_ERR_INVALID";
+        case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED";
+        case ATTN_ERR_HIP: return "ATTN_ERR_HIP";
+        case ATTN_ERR_NOMEM: return "ATTN_ERR_NOMEM";
+    }
+    return "ATTN_ERR_UNKNOWN";
+}
+
+attn_status attn_fwd_plan_info(const attn_fwd_plan *plan, int64_t *grid, int32_t *block,
+                               int32_t *tile_q, int32_t *tile_k, int32_t *lds_bytes) {
+    if (!plan) return ATTN_ERR_INVALID;
+    if (grid) *grid = plan->grid;
+    if (block) *block = plan->block;
+    if (tile_q) *tile_q = plan->tile_q;
+    if (tile_k) *tile_k = plan->tile_k;
+    if (lds_bytes) *lds_bytes = plan->lds_bytes;
+    return ATTN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,184 @@
+#!/usr/bin/env python3
+"""Attention-forward benchmark on one MI355X.
+
+One step = one attention forward pass (every stage of the fused kernel) over
+the long-sequence workload: B=1, H_q=32, H_kv=8, N=16384, d=128, causal, bf16,
+K scaled by 2. Inputs are generated once and are resident in HBM before the
+timed region. Prints ONE JSON line.
+
+  value       = algorithmic FLOPs / wall time per step (TFLOP/s), with the
+                FLOPs 2·B·H_q·N_q·N_kv·(d_qk + d_v), halved when causal
+  roofline    = the kernel's own launch time, from HIP events recorded on the
+                stream the kernel is launched on, against the bf16 dense MFMA
+                peak (256 CUs x 4096 flop/clk x 2.4 GHz = 2516.6 TFLOP/s)
+  cpu_baseline= the fp64 oracle timed on the host over a bounded row sample
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12  # 2516.6
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_C4_traffic.json")
+METRIC = "attention fwd TFLOP/s on 1 MI355X + % of bf16 MFMA peak (causal FLOPs /2)"
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "accelerator_programming_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.startswith("attn_fwd") or name == "tile.hpp":
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for_current_kernel(workload_name: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when it was taken on other kernel sources or another workload."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sha") != kernel_source_sha() or t.get("workload") != workload_name:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, target_s: float, threads: int):
+    """Time the oracle on a sample of rows sized for roughly target_s seconds."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from accelerator_programming_amd.inputs import sample_rows
+
+    Q = q.float().cpu().numpy()
+    K = k.float().cpu().numpy()
+    V = v.float().cpu().numpy() if not w.v_from_k else np.ascontiguousarray(
+        k[..., : w.dv].float().cpu().numpy())
+
+    def row_flops(rows):
+        keys = (rows[:, 2] + 1) if w.causal else torch.full((rows.shape[0],), w.Nkv)
+        return float((2.0 * keys.double() * (w.dqk + w.dv)).sum())
+
+    def timed(n):
+        rows = sample_rows(w, n, seed=123)
+        t0 = time.perf_counter()
+        _, _, used = oracle.attention_fp64(Q, K, V, w.causal, w.softmax_scale, rows=rows,
+                                           threads=threads)
+        return time.perf_counter() - t0, row_flops(rows), used, rows.shape[0]
+
+    dt, fl, used, n = timed(max(threads * 4, 64))
+    n2 = int(min(max(n * target_s / max(dt, 1e-3), n), 200000))
+    dt, fl, used, n = timed(n2)
+    return {
+        "value": fl / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": used,
+        "kind": "oracle",
+        "sample": "%d seeded (b,h,i) rows of %s, each row's unmasked keys only; %.1f s wall, "
+                  "%.3g FLOP" % (n, w.name, dt, fl),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="C4", help="workload C1..C5 (the metric is quoted on C4)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(asked for --gpus %d)" % args.gpus, file=sys.stderr)
+        return 2
+
+    import torch
+
+    from accelerator_programming_amd import attn
+    from accelerator_programming_amd.inputs import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.config]
+    torch.cuda.set_device(0)
+    q, k, v = make_inputs(w, "cuda")
+    B, Hq, N = w.B, w.Hq, w.Nq
+    o = torch.empty((B, Hq, N, w.dv), dtype=q.dtype, device="cuda")
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device="cuda")
+    op = attn.AttnFwd(q, k, v, w.causal, w.softmax_scale, o)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        op.run(q, k, v, o, lse, stream=stream)
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        op.run(q, k, v, o, lse, stream=stream)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    op.close()
+
+    kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    kern_avg_ms = sum(kern_ms) / len(kern_ms)
+    ms_per_step = wall * 1e3 / args.steps
+    flops = w.flops()
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (kern_avg_ms * 1e-3) / 1e12
+    finite = bool(torch.isfinite(o).all().item() and torch.isfinite(lse).all().item())
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        threads = min(16, len(os.sched_getaffinity(0)))
+        cpu = cpu_baseline(w, q, k, v, args.cpu_seconds, threads)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == torch.bfloat16 else "fp32-in/bf16-mfma",
+        "data": "synthetic (seeded N(0,1) inputs, resident in HBM)",
+        "config": {"workload": w.name, "B": w.B, "H_q": w.Hq, "H_kv": w.Hkv, "N_q": w.Nq,
+                   "N_kv": w.Nkv, "d_qk": w.dqk, "d_v": w.dv, "causal": w.causal,
+                   "gflop_per_step": round(flops / 1e9, 3), "parallelism": "single-gpu",
+                   "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+                   "outputs_finite": finite},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_for_current_kernel(w.name),
+                     "kernel_ms_avg": round(kern_avg_ms, 4),
+                     "kernel": "attn::attn_fwd_kernel<%d, %s, %s>" % (
+                         w.dqk, "true" if w.causal else "false",
+                         "__bf16" if w.dtype == torch.bfloat16 else "float")},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0 if finite else 1
+
+
+if __name__ == "__main__":
+    sys.exit(main())

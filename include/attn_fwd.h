@@ -1,0 +1,122 @@
+/*
+ * attn_fwd.h - C ABI of the MI355X (gfx950) fused attention forward library.
+ *
+ * The operation is attention forward written as a stream of tiles:
+ *   S = Q·Kᵀ·scale, an optional causal mask, a row softmax done online across
+ *   K/V tiles (exp -> sum -> divide), O = P·V, plus the per-row logsumexp.
+ * Sources: "CS149 L11: Programming Specialized Hardware" (quidproquo.cc),
+ * section 5 (slide 48: softmax as Map(exp) -> Reduce(+) -> Zip(/); slide 54:
+ * FlashAttention as the chain Q·Kᵀ, Mask, Softmax, Dropout, ×V) and section 6
+ * (the decoder's Q·Kᵀ, scale, mask, softmax, ×V); "Distilling a 4.5 hour CUDA
+ * talk" (levidiamode.com), section 7 (Q resident, K/V streamed through on-chip
+ * memory, running max and normalizer).
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are 4-D [B, H, N, d] with the innermost (d) stride 1. Their
+ *     (b, h, n) strides are given in elements; a zero stride triple means
+ *     "contiguous". Every stride and every base pointer must be 16-byte
+ *     aligned (a multiple of 8 elements for bf16, 4 for fp32).
+ *   - Q is [B, H_q, N, d], K is [B, H_kv, N_kv, d], V is [B, H_kv, N_kv, d_v],
+ *     O is [B, H_q, N, d_v]; logsumexp is [B, H_q, N] fp32, contiguous.
+ *     Query head h reads K/V head h / (H_q / H_kv) (contiguous GQA groups).
+ *   - causal masks key j for query row i when j > i (top-left alignment) and
+ *     needs N_kv == N. Dropout is not applied (probability 0).
+ *   - logsumexp[b,h,i] = ln(sum_j exp(scale * q_i·k_j)) over unmasked keys.
+ *   - All device buffers are owned by the caller, who keeps them alive until
+ *     the work queued on the stream has finished. The library allocates no
+ *     device memory.
+ *   - Every function returns a status code; nothing throws or aborts across
+ *     the ABI.
+ */
+#ifndef ATTN_FWD_H
+#define ATTN_FWD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct attn_fwd_plan attn_fwd_plan; /* opaque, host-side, immutable */
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_INVALID = 1,     /* malformed argument (sizes, strides, pointers) */
+    ATTN_ERR_UNSUPPORTED = 2, /* well-formed but no kernel variant serves it */
+    ATTN_ERR_HIP = 3,         /* the HIP runtime reported an error at launch */
+    ATTN_ERR_NOMEM = 4        /* host allocation of the plan failed */
+} attn_status;
+
+typedef enum {
+    ATTN_BF16 = 0, /* Q, K, V and O in bf16 */
+    ATTN_FP32 = 1  /* Q, K, V and O in fp32; the tiles are rounded to bf16
+                      (round-to-nearest-even) before the MFMA contractions */
+} attn_dtype;
+
+typedef struct {
+    int64_t B, H_q, H_kv;
+    int64_t N;        /* query rows per head (N_q) */
+    int64_t d;        /* head dimension of Q and K (d_qk) */
+    int64_t N_kv;     /* key/value rows per head; 0 means N */
+    int64_t d_v;      /* head dimension of V and O; 0 means d */
+    int32_t causal;   /* 0 or 1 */
+    float scale;      /* softmax scale, finite and > 0 (e.g. 1/sqrt(d)) */
+    int32_t dtype;    /* attn_dtype */
+    int64_t q_strides[3], k_strides[3], v_strides[3], o_strides[3]; /* (b,h,n) */
+} attn_fwd_params;
+
+/*
+ * attn_fwd_create - validate a problem and choose its kernel variant.
+ * Arguments are the problem of the whole library: B, H_q, H_kv, N, d, causal
+ * and scale, with bf16 tensors, contiguous [B, H, N, d] layout, N_kv = N and
+ * d_v = d. On success *plan receives a new plan (free it with
+ * attn_fwd_destroy). Makes no HIP call. Returns ATTN_ERR_INVALID for
+ * non-positive sizes, H_q not a multiple of H_kv, a non-finite or
+ * non-positive scale, or plan == NULL; ATTN_ERR_UNSUPPORTED for head
+ * dimensions without a kernel (supported: d = 64 and d = 128).
+ */
+attn_status attn_fwd_create(attn_fwd_plan **plan, int64_t B, int64_t H_q, int64_t H_kv,
+                            int64_t N, int64_t d, int32_t causal, float scale);
+
+/*
+ * attn_fwd_create_ex - as attn_fwd_create, from a full descriptor: adds N_kv,
+ * d_v, the dtype and explicit strides. Extra ATTN_ERR_INVALID cases: causal
+ * with N_kv != N, strides that are not 16-byte multiples, row strides below
+ * the row width, or a tensor whose [N, d] slab exceeds 2^31 elements.
+ * Supported (d, d_v, dtype): (64, 64, bf16), (128, 128, bf16),
+ * (64, 64, fp32).
+ */
+attn_status attn_fwd_create_ex(const attn_fwd_params *params, attn_fwd_plan **plan);
+
+/*
+ * attn_fwd_run - queue the attention forward pass on `stream` (a hipStream_t;
+ * NULL is the default stream). Q, K, V, O are device pointers with the plan's
+ * dtype and strides; lse is a device pointer to B*H_q*N floats, or NULL to
+ * skip writing logsumexp. V may alias K (e.g. V = the first d_v columns of K
+ * through its strides). Returns immediately; never synchronizes. Returns
+ * ATTN_ERR_INVALID for a NULL plan or tensor pointer or a pointer that is not
+ * 16-byte aligned (checked before any HIP call), ATTN_ERR_HIP if the launch
+ * fails.
+ */
+attn_status attn_fwd_run(const attn_fwd_plan *plan, const void *Q, const void *K,
+                         const void *V, void *O, float *lse, void *stream);
+
+/* attn_fwd_destroy - free a plan. NULL is accepted and ignored. */
+void attn_fwd_destroy(attn_fwd_plan *plan);
+
+/* attn_status_str - a static, human-readable name for a status code. */
+const char *attn_status_str(attn_status status);
+
+/*
+ * attn_fwd_plan_info - launch geometry chosen by a plan, for tests and
+ * reports: workgroups in the grid, threads per workgroup, query rows and key
+ * rows per tile, and LDS bytes per workgroup. Any output pointer may be NULL.
+ */
+attn_status attn_fwd_plan_info(const attn_fwd_plan *plan, int64_t *grid, int32_t *block,
+                               int32_t *tile_q, int32_t *tile_k, int32_t *lds_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_FWD_H */

@@ -1,0 +1,162 @@
+"""The C-ABI boundary on the host: the library loads, exports every function
+include/attn_fwd.h declares, and validates its arguments before any HIP call
+(so these tests run without a GPU)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from accelerator_programming_amd import attn
+from accelerator_programming_amd.attn import (ATTN_BF16, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED,
+                                              ATTN_FP32, ATTN_OK, AttnError, AttnFwdParams)
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_fwd.h")
+SELFTEST = os.path.join(ROOT, "accelerator_programming_amd", "libattn_tile_selftest.so")
+
+
+def declared_functions(path):
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions(HEADER)
+    for n in ("attn_fwd_create", "attn_fwd_run", "attn_fwd_destroy"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = attn.lib()
+    for name in declared_functions(HEADER):
+        assert hasattr(L, name), name
+
+
+def test_selftest_library_loads():
+    L = ctypes.CDLL(SELFTEST)
+    for n in ("tile_selftest_mfma", "tile_selftest_xhalf", "tile_selftest_pv", "tile_selftest_tr16"):
+        assert hasattr(L, n)
+
+
+def test_params_struct_matches_header_layout():
+    # 7 int64 + int32 + float + int32 (+4 padding) + 4 x 3 int64
+    assert ctypes.sizeof(AttnFwdParams) == 7 * 8 + 4 + 4 + 4 + 4 + 12 * 8
+
+
+def create(**kw):
+    """Call the C entry point directly (the Python helper normalises causal)."""
+    base = dict(B=1, H_q=2, H_kv=1, N=256, d=128, causal=1, scale=1 / math.sqrt(128))
+    base.update(kw)
+    plan = ctypes.c_void_p()
+    st = attn.lib().attn_fwd_create(ctypes.byref(plan), base["B"], base["H_q"], base["H_kv"],
+                                    base["N"], base["d"], base["causal"], base["scale"])
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_create")
+    return plan.value
+
+
+def status_of(fn):
+    try:
+        plan = fn()
+    except AttnError as e:
+        return e.status
+    attn.attn_fwd_destroy(plan)
+    return ATTN_OK
+
+
+@pytest.mark.parametrize("kw,expected", [
+    ({}, ATTN_OK),
+    (dict(d=64), ATTN_OK),
+    (dict(B=0), ATTN_ERR_INVALID),
+    (dict(H_q=0), ATTN_ERR_INVALID),
+    (dict(N=0), ATTN_ERR_INVALID),
+    (dict(N=-5), ATTN_ERR_INVALID),
+    (dict(H_q=3, H_kv=2), ATTN_ERR_INVALID),
+    (dict(scale=float("nan")), ATTN_ERR_INVALID),
+    (dict(scale=float("inf")), ATTN_ERR_INVALID),
+    (dict(scale=0.0), ATTN_ERR_INVALID),
+    (dict(scale=-0.1), ATTN_ERR_INVALID),
+    (dict(causal=2), ATTN_ERR_INVALID),
+    (dict(d=96), ATTN_ERR_UNSUPPORTED),
+    (dict(d=256), ATTN_ERR_UNSUPPORTED),
+])
+def test_create_validation(kw, expected):
+    assert status_of(lambda: create(**kw)) == expected
+
+
+def ex_params(**kw):
+    p = AttnFwdParams()
+    p.B, p.H_q, p.H_kv, p.N, p.d = 2, 4, 2, 300, 64
+    p.N_kv, p.d_v = 0, 0
+    p.causal, p.scale, p.dtype = 0, 0.125, ATTN_BF16
+    for k, v in kw.items():
+        if k.endswith("_strides"):
+            setattr(p, k, (ctypes.c_int64 * 3)(*v))
+        else:
+            setattr(p, k, v)
+    return p
+
+
+@pytest.mark.parametrize("kw,expected", [
+    ({}, ATTN_OK),
+    (dict(N_kv=517), ATTN_OK),
+    (dict(dtype=ATTN_FP32), ATTN_OK),
+    (dict(dtype=ATTN_FP32, d=128), ATTN_ERR_UNSUPPORTED),
+    (dict(dtype=7), ATTN_ERR_INVALID),
+    (dict(causal=1, N_kv=301), ATTN_ERR_INVALID),
+    (dict(d_v=32), ATTN_ERR_UNSUPPORTED),
+    # V as the first 64 columns of a 128-wide row: legal strides
+    (dict(v_strides=(2 * 300 * 128, 300 * 128, 128)), ATTN_OK),
+    # row stride smaller than the row
+    (dict(q_strides=(4 * 300 * 64, 300 * 64, 56)), ATTN_ERR_INVALID),
+    # a stride that breaks 16-byte alignment of bf16 rows
+    (dict(k_strides=(2 * 300 * 68, 300 * 68, 68)), ATTN_ERR_INVALID),
+    (dict(o_strides=(-1, 300 * 64, 64)), ATTN_ERR_INVALID),
+])
+def test_create_ex_validation(kw, expected):
+    p = ex_params(**kw)
+    assert status_of(lambda: attn.attn_fwd_create_ex(p)) == expected
+
+
+def test_create_null_plan_pointer():
+    L = attn.lib()
+    assert L.attn_fwd_create(None, 1, 1, 1, 128, 64, 0, 0.125) == ATTN_ERR_INVALID
+    assert L.attn_fwd_create_ex(None, None) == ATTN_ERR_INVALID
+
+
+def test_destroy_null_is_safe():
+    attn.attn_fwd_destroy(None)
+
+
+def test_plan_info_geometry():
+    plan = attn.attn_fwd_create(2, 32, 8, 4096, 128, 1, 1 / math.sqrt(128))
+    try:
+        info = attn.attn_fwd_plan_info(plan)
+    finally:
+        attn.attn_fwd_destroy(plan)
+    assert info["grid"] == 2 * 32 * (4096 // info["tile_q"])
+    assert info["block"] % 64 == 0
+    assert info["lds_bytes"] <= 160 * 1024
+
+
+def test_run_rejects_null_and_misaligned_pointers_before_launch():
+    plan = create()
+    try:
+        L = attn.lib()
+        assert L.attn_fwd_run(None, 16, 16, 16, 16, None, None) == ATTN_ERR_INVALID
+        assert L.attn_fwd_run(plan, None, 16, 16, 16, None, None) == ATTN_ERR_INVALID
+        assert L.attn_fwd_run(plan, 16, 16, 16, None, None, None) == ATTN_ERR_INVALID
+        assert L.attn_fwd_run(plan, 16 + 2, 16, 16, 16, None, None) == ATTN_ERR_INVALID
+        assert L.attn_fwd_run(plan, 16, 16, 16 + 8, 16, None, None) == ATTN_ERR_INVALID
+        assert L.attn_fwd_run(plan, 16, 16, 16, 16, 18, None) == ATTN_ERR_INVALID
+    finally:
+        attn.attn_fwd_destroy(plan)
+
+
+def test_status_strings():
+    assert attn.attn_status_str(ATTN_OK) == "ATTN_OK"
+    assert attn.attn_status_str(ATTN_ERR_UNSUPPORTED) == "ATTN_ERR_UNSUPPORTED"
+    assert attn.attn_status_str(99) == "ATTN_ERR_UNKNOWN"

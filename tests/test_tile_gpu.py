@@ -1,0 +1,64 @@
+"""Tile-layer probes on the GPU: each primitive the attention kernel is built
+from, checked bit-exactly with inputs whose products are exact in fp32."""
+import ctypes
+import os
+
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SELFTEST = os.path.join(ROOT, "accelerator_programming_amd", "libattn_tile_selftest.so")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    L = ctypes.CDLL(SELFTEST)
+    for n in ("tile_selftest_mfma", "tile_selftest_xhalf", "tile_selftest_pv"):
+        getattr(L, n).restype = ctypes.c_int
+        getattr(L, n).argtypes = [ctypes.c_void_p] * 4
+    return L
+
+
+def stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def small_ints(shape, seed, lo=-4, hi=5):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randint(lo, hi, shape, generator=g).float()
+
+
+def test_mfma_32x32x16_fragment_layout(lib):
+    A = small_ints((32, 16), 1)
+    B = small_ints((16, 32), 2)
+    Ad, Bd = A.bfloat16().cuda(), B.bfloat16().cuda()
+    C = torch.full((32, 32), float("nan"), device="cuda")
+    assert lib.tile_selftest_mfma(Ad.data_ptr(), Bd.data_ptr(), C.data_ptr(), stream()) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(C.cpu(), A @ B)
+
+
+def test_cross_half_max_and_sum(lib):
+    x = small_ints((64,), 3, -100, 100) / 8
+    xd = x.cuda()
+    mx = torch.empty(64, device="cuda")
+    sm = torch.empty(64, device="cuda")
+    assert lib.tile_selftest_xhalf(xd.data_ptr(), mx.data_ptr(), sm.data_ptr(), stream()) == 0
+    torch.cuda.synchronize()
+    other = x.roll(32)
+    assert torch.equal(mx.cpu(), torch.maximum(x, other))
+    assert torch.equal(sm.cpu(), x + other)
+
+
+def test_pv_through_permuted_vt(lib):
+    # St[key][query] in the accumulator layout; P = St^T rounded to bf16 (exact
+    # here: quarter-integers), V small integers -> O = P·V exact in fp32.
+    St = small_ints((32, 32), 4) / 4
+    V = small_ints((32, 32), 5)
+    Sd, Vd = St.cuda(), V.bfloat16().cuda()
+    O = torch.full((32, 32), float("nan"), device="cuda")
+    assert lib.tile_selftest_pv(Sd.data_ptr(), Vd.data_ptr(), O.data_ptr(), stream()) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(O.cpu(), St.t() @ V)
