@@ -11,25 +11,32 @@
 // gfx950 mapping
 //  * 4 waves of 64 lanes; wave w owns query rows q0 + 32w .. q0 + 32w + 31.
 //  * Scores are computed transposed, Sᵀ = K·Qᵀ, with 32x32x16 bf16 MFMAs:
-//    A = a 32-key slab of K from LDS, B = the wave's Q fragment held in VGPRs.
-//    In the accumulator every lane then holds one query row (l % 32) and 16
-//    keys, so the row max and row sum are in-lane, plus one swap with lane
-//    l ^ 32 per tile for the max.
+//    A = a 32-key slab of K read from LDS, B = the wave's Q fragment held in
+//    VGPRs for the whole loop. In the accumulator every lane then holds one
+//    query row (l % 32) and 16 keys, so the row max and row sum are in-lane,
+//    plus one swap with lane l ^ 32 per tile for the max.
 //  * Oᵀ += Vᵀ·Pᵀ: Pᵀ is the score accumulator converted to bf16 in place.
 //    The keys a lane holds come in runs of four (rows 8*(r/4) + 4g + r%4), so
 //    the MFMA k index 8g + e names key 8*(e/4) + 4g + e%4 of each 16-key
-//    chunk: bits 2 and 3 swapped. Vᵀ is written to LDS with its keys in that
-//    same order, which makes P·V correct with no data movement for P.
+//    chunk. The Vᵀ operand is read from the row-major V tile with the LDS
+//    transpose read (ds_read_b64_tr_b16), two reads of four keys each, in
+//    exactly that key order: P needs no data movement, V no transposing
+//    store. (The pages' P·V operand is likewise transposed at load time.)
 //  * Softmax in base 2 with log2(e) folded into the scale on the host, and
 //    one reciprocal per row at the end ("Distilling a 4.5 hour CUDA talk",
 //    section 2 on the base-2 exponential and on reciprocal reuse; section 7
-//    on folding log2(e) into the temperature).
-//  * K/V staging: every wave loads a share of tile t+1 into VGPRs before it
-//    computes tile t, then writes it to the other LDS buffer; one barrier per
-//    tile separates "buffer full" from "buffer free". K keeps row-major order
-//    with rows padded by 16 bytes; V is transposed on its way into LDS
-//    (the transpose happens at load time, as the pages describe for the
-//    P·V operand), rows padded by 16 bytes.
+//    on folding log2(e) into the temperature). The running max is raised
+//    lazily: O and l are rescaled only when some row's tile max exceeds its
+//    running max by more than 2^kLazy, which keeps every p <= 2^kLazy and
+//    leaves O = acc / l and lse = m + log2 l exact in real arithmetic.
+//  * K/V staging: every wave issues LDS-DMA loads (global_load_lds_dwordx4,
+//    no VGPRs) for its share of tile t+1 into the other LDS buffer before it
+//    computes tile t; then "my loads landed" (s_waitcnt vmcnt(0)) and one
+//    barrier per tile ("everyone's loads landed, nobody reads the old
+//    buffer") close the iteration. LDS-DMA writes 16 bytes per lane at
+//    consecutive addresses, so bank-conflict avoidance is an XOR swizzle of
+//    the 16-byte chunks of a row, applied by choosing which global chunk each
+//    lane fetches (XOR layouts: "Distilling a 4.5 hour CUDA talk", section 8).
 #pragma once
 #include "tile.hpp"
 
@@ -52,34 +59,29 @@ struct TileCfg {
     static constexpr int TK = 64;           // keys per streamed tile
     static constexpr int NWAVE = 4;
     static constexpr int NT = 64 * NWAVE;   // threads per workgroup
-    static constexpr int PK = D + 8;        // K row pitch in LDS (elements)
-    static constexpr int PV = TK + 8;       // Vᵀ row pitch in LDS (elements)
-    static constexpr int K_ELEMS = TK * PK;
-    static constexpr int V_ELEMS = D * PV;
-    static constexpr int STAGE = K_ELEMS + V_ELEMS;
-    static constexpr int LDS_BYTES = 2 * STAGE * 2;
-    static constexpr int KCH = TK * D / 8 / NT;   // 16-byte K chunks per thread
-    static constexpr int VITEMS = (TK / 4) * (D / 8);  // 4-key x 8-column V items
-    static_assert(TK * D / 8 % NT == 0, "K tile must split evenly over the threads");
-    static_assert(VITEMS <= NT, "one V item per thread at most");
+    static constexpr int CPR = D / 8;       // 16-byte chunks per K or V row
+    static constexpr int TILE_ELEMS = TK * D;
+    static constexpr int STAGE = 2 * TILE_ELEMS;             // K tile then V tile
+    static constexpr int LDS_BYTES = 2 * STAGE * 2;          // two stages, bf16
+    static constexpr int ROWS_PER_DMA = 64 / CPR;            // rows one wave-wide DMA covers
+    static constexpr int DMA_PER_WAVE = TK / ROWS_PER_DMA / NWAVE;  // per tile per K (or V)
+    static_assert(TK % (ROWS_PER_DMA * NWAVE) == 0, "tile rows must split over the waves");
 };
-
-// Position in the LDS Vᵀ row of key `key` (0..TK-1): bits 2 and 3 swapped.
-__device__ __forceinline__ int vt_pos(int key) {
-    return (key & ~0xC) | ((key & 4) << 1) | ((key & 8) >> 1);
-}
 
 // Two workgroups per CU (two waves per SIMD): the register budget per wave is
 // therefore 256, and one wave's softmax can issue while the other's MFMAs run.
 template <int D, bool CAUSAL, typename TIn>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_kernel(const KernelArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
     using C = TileCfg<D>;
-    constexpr int TQ = C::TQ, TK = C::TK, NT = C::NT, PK = C::PK, PV = C::PV;
-    __shared__ __attribute__((aligned(16))) __bf16 lds[2 * C::STAGE];
+    constexpr int TQ = C::TQ, TK = C::TK, CPR = C::CPR;
+    constexpr float kLazy = 8.0f;
+    __shared__ __attribute__((aligned(1024))) __bf16 lds[2 * C::STAGE];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, g = lane >> 5;
 
     // ---- work item: heaviest causal tiles are dispatched first -------------
@@ -108,51 +110,27 @@ attn_fwd_kernel(const KernelArgs a) {
         qf[kc] = u32x4_as_bf16x8(v);
     }
 
-    // ---- staging registers for the next K/V tile ---------------------------
-    u32x4 kreg[C::KCH];
-    u32x4 vreg[4];
-    const int v_kq = tid % (TK / 4);  // which 4-key group of the tile
-    const int v_do = tid / (TK / 4);  // which 8-column group of V
-    const bool v_active = tid < C::VITEMS;
-
-    auto load_tile = [&](int t) {
-        const int kb0 = t * TK;
-#pragma unroll
-        for (int u = 0; u < C::KCH; ++u) {
-            const int ch = tid + NT * u;
-            const int r = ch / (D / 8), c8 = ch % (D / 8);
-            const int key = kb0 + r;
-            kreg[u] = u32x4{0, 0, 0, 0};
-            if (key < a.Nkv) kreg[u] = load8_bf16(Kp + (int64_t)key * a.k_sn + 8 * c8);
-        }
-        if (v_active) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int key = kb0 + 4 * v_kq + j;
-                vreg[j] = u32x4{0, 0, 0, 0};
-                if (key < a.Nkv) vreg[j] = load8_bf16(Vp + (int64_t)key * a.v_sn + 8 * v_do);
-            }
-        }
-    };
-    auto store_tile = [&](int s) {
+    // ---- LDS-DMA of one K/V tile: each wave fills DMA_PER_WAVE windows of
+    // 64 lanes x 16 bytes in each tile; lane i of a window lands at chunk i. --
+    const int dma_r = lane / CPR;          // row within the window
+    const int dma_p = lane % CPR;          // physical chunk this lane fills
+    auto issue_tile = [&](int t, int s) {
         __bf16 *Ks = lds + s * C::STAGE;
-        __bf16 *Vs = Ks + C::K_ELEMS;
+        __bf16 *Vs = Ks + C::TILE_ELEMS;
 #pragma unroll
-        for (int u = 0; u < C::KCH; ++u) {
-            const int ch = tid + NT * u;
-            const int r = ch / (D / 8), c8 = ch % (D / 8);
-            *(u32x4 *)(Ks + r * PK + 8 * c8) = kreg[u];
-        }
-        if (v_active) {
-            // 4 keys x 8 columns in registers -> 8 Vᵀ rows x 4 keys in LDS
-            const int pos = vt_pos(4 * v_kq);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int p = i >> 1;
-                const bool hi = i & 1;
-                const uint32_t k01 = pick_halves(vreg[0][p], vreg[1][p], hi);
-                const uint32_t k23 = pick_halves(vreg[2][p], vreg[3][p], hi);
-                *(u32x2 *)(Vs + (8 * v_do + i) * PV + pos) = u32x2{k01, k23};
+        for (int u = 0; u < C::DMA_PER_WAVE; ++u) {
+            const int r = (w * C::DMA_PER_WAVE + u) * C::ROWS_PER_DMA + dma_r;  // tile row
+            const int key = min(t * TK + r, a.Nkv - 1);  // clamped: a finite, masked row
+            const TIn *kg = Kp + (int64_t)key * a.k_sn + 8 * k_chunk<D>(r, dma_p);
+            const TIn *vg = Vp + (int64_t)key * a.v_sn + 8 * v_chunk<D>(r, dma_p);
+            const int win = (w * C::DMA_PER_WAVE + u) * 64 * 8;  // elements
+            if constexpr (sizeof(TIn) == 2) {
+                __builtin_amdgcn_global_load_lds(kg, (lds_void *)(Ks + win), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(vg, (lds_void *)(Vs + win), 16, 0, 0);
+            } else {
+                // fp32 inputs: round to bf16 in registers, same LDS placement
+                *(u32x4 *)(Ks + win + 8 * lane) = load8_bf16(kg);
+                *(u32x4 *)(Vs + win + 8 * lane) = load8_bf16(vg);
             }
         }
     };
@@ -163,24 +141,24 @@ attn_fwd_kernel(const KernelArgs a) {
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-    float m = -INFINITY;  // running max of score * c (base-2 domain)
+    float m = -INFINITY;  // running max of score * c (base-2 domain), raised lazily
     float l = 0.f;        // running normalizer, partial over this lane's keys
 
-    if (n_tiles > 0) {
-        load_tile(0);
-        store_tile(0);
-    }
+    if (n_tiles > 0) issue_tile(0, 0);
+    __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's DMA landed
     __syncthreads();
 
     for (int t = 0; t < n_tiles; ++t) {
         const int s = t & 1;
-        if (t + 1 < n_tiles) load_tile(t + 1);
+        if (t + 1 < n_tiles) issue_tile(t + 1, s ^ 1);
 
         const int kb0 = t * TK;
-        const bool wave_active = !CAUSAL || kb0 <= wrow0 + 31;
-        if (wave_active) {
+        {
+            // (A wave whose rows see no key of this tile still runs it: the
+            // mask zeroes its p, and a uniform path keeps the accumulators in
+            // place; such tiles are under 1% of a long causal sweep.)
             const __bf16 *Ks = lds + s * C::STAGE;
-            const __bf16 *Vs = Ks + C::K_ELEMS;
+            const __bf16 *Vs = Ks + C::TILE_ELEMS;
 
             // Sᵀ = K·Qᵀ for the 64 keys of this tile, two 32-key slabs
             f32x16 sacc[2];
@@ -188,10 +166,10 @@ attn_fwd_kernel(const KernelArgs a) {
             for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+                const int kr = 32 * kb + l32;
 #pragma unroll
                 for (int kc = 0; kc < D / 16; ++kc) {
-                    const bf16x8 kf = *(const bf16x8 *)(Ks + (32 * kb + l32) * PK + 16 * kc + 8 * g);
-                    sacc[kb] = mfma_32x32x16(kf, qf[kc], sacc[kb]);
+                    sacc[kb] = mfma_32x32x16(k_frag<D>(Ks, kr, kc, g), qf[kc], sacc[kb]);
                 }
             }
 
@@ -208,57 +186,54 @@ attn_fwd_kernel(const KernelArgs a) {
             }
 
             // row max: in-lane over 32 keys, then across the two wave halves
-            float mx = sacc[0][0];
+            float mx = fmaxf(sacc[0][0], sacc[0][1]);
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[0][r], sacc[0][r + 1]));
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-            mx = xhalf_max(mx);
-            const float m_new = fmaxf(m, mx * a.c);
-            const float m_sub = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = exp2_hw(m - m_sub);
-            m = m_new;
+            for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[1][r], sacc[1][r + 1]));
+            mx = xhalf_max(mx) * a.c;
 
-            // p = 2^(s·c - m): Map(exp); partial row sum: Reduce(+)
-            float ls = 0.f;
+            // lazy rescale: only when some row's max grew by more than 2^kLazy
+            if (__builtin_amdgcn_ballot_w64(mx > m + kLazy)) {
+                const float m_new = fmaxf(m, mx);
+                const float alpha = (m_new == -INFINITY) ? 1.f : exp2_hw(m - m_new);
+                l *= alpha;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+                for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float p = exp2_hw(fmaf(sacc[kb][r], a.c, -m_sub));
-                    sacc[kb][r] = p;
-                    ls += p;
-                }
-            l = alpha * l + ls;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+                    for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+                m = m_new;
+            }
+            const float m_sub = (m == -INFINITY) ? 0.f : m;
 
+            // p = 2^(s·c - m): Map(exp); partial row sum: Reduce(+);
             // Pᵀ as bf16 B operands: 16-key chunk 2*kb + hh is registers 8hh..8hh+7
             bf16x8 pf[4];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
+                    float p[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        p[e] = exp2_hw(fmaf(sacc[kb][8 * hh + e], a.c, -m_sub));
+                        l += p[e];
+                    }
                     u32x4 v;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        v[e] = pack_bf16x2(sacc[kb][8 * hh + 2 * e], sacc[kb][8 * hh + 2 * e + 1]);
+                    for (int e = 0; e < 4; ++e) v[e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
                     pf[2 * kb + hh] = u32x4_as_bf16x8(v);
                 }
 
-            // Oᵀ += Vᵀ·Pᵀ
+            // Oᵀ += Vᵀ·Pᵀ, Vᵀ fragments by transpose reads of the row-major V tile
 #pragma unroll
             for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-                for (int kc = 0; kc < TK / 16; ++kc) {
-                    const bf16x8 vf = *(const bf16x8 *)(Vs + (32 * db + l32) * PV + 16 * kc + 8 * g);
-                    oacc[db] = mfma_32x32x16(vf, pf[kc], oacc[db]);
-                }
+                for (int kc = 0; kc < TK / 16; ++kc)
+                    oacc[db] = mfma_32x32x16(vt_frag<D>(Vs, db, kc, lane), pf[kc], oacc[db]);
         }
 
-        if (t + 1 < n_tiles) store_tile(s ^ 1);
+        __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's DMA of tile t+1 landed
         __syncthreads();
     }
 
@@ -278,6 +253,7 @@ attn_fwd_kernel(const KernelArgs a) {
         if (g == 0 && a.lse)
             a.lse[((int64_t)b * a.Hq + h) * a.Nq + row] = (m + log2f(l_row)) * 0.69314718055994531f;
     }
+#endif
 }
 
 }  // namespace attn

@@ -47,10 +47,12 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 // 2^x on the transcendental unit (v_exp_f32). exp2(-inf) = 0.
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> two bf16, round to nearest even: one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    __bf16 a = (__bf16)lo, b = (__bf16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 __device__ __forceinline__ bf16x8 u32x4_as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -64,18 +66,66 @@ __device__ __forceinline__ u32x4 load8_bf16(const float *p) {
                  pack_bf16x2(b[2], b[3])};
 }
 
-// Select the low (hi = false) or high 16-bit halves of two dwords into one
-// dword: result = half(lo_src) | half(hi_src) << 16 (one v_perm_b32).
-__device__ __forceinline__ uint32_t pick_halves(uint32_t lo_src, uint32_t hi_src, bool hi) {
-    return __builtin_amdgcn_perm(hi_src, lo_src, hi ? 0x07060302u : 0x05040100u);
-}
-
 // Stores of four consecutive output values.
 __device__ __forceinline__ void store4(__bf16 *p, float a, float b, float c, float d) {
     *(u32x2 *)p = u32x2{pack_bf16x2(a, b), pack_bf16x2(c, d)};
 }
 __device__ __forceinline__ void store4(float *p, float a, float b, float c, float d) {
     *(f32x4 *)p = f32x4{a, b, c, d};
+}
+
+// ---------------------------------------------------------------------------
+// LDS tile layouts. K and V tiles are row-major, D bf16 per row, no padding;
+// the 16-byte chunks of each row are XOR-permuted ("Distilling a 4.5 hour CUDA
+// talk", section 8: a swizzle is an invertible permutation within a row that
+// spreads the accesses a layout sees across banks, XOR being its own inverse).
+// ---------------------------------------------------------------------------
+
+// Physical chunk of logical chunk c in K row r: XOR with the row, so the 8
+// (or 16) consecutive rows an A-fragment read touches hit distinct banks.
+template <int D>
+__device__ __forceinline__ int k_chunk(int r, int c) { return c ^ (r & (D / 8 - 1)); }
+
+// Physical chunk of logical chunk c in V row r. A transpose read covers four
+// consecutive rows x 32 bytes per 16 lanes (x 64 bytes per 32 lanes); the XOR
+// value 2q + 8*parity(q), q = r % 4, keeps both windows conflict-free.
+template <int D>
+__device__ __forceinline__ int v_chunk(int r, int c) {
+    const int q = r & 3;
+    const int f = (D >= 128) ? (2 * q + 8 * ((q ^ (q >> 1)) & 1)) : 2 * q;
+    return c ^ f;
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// A operand of Sᵀ = K·Qᵀ: K row kr, d = 16kc + 8g .. +7 (one ds_read_b128).
+template <int D>
+__device__ __forceinline__ bf16x8 k_frag(const __bf16 *Ks, int kr, int kc, int g) {
+    return *(const bf16x8 *)(Ks + kr * D + 8 * k_chunk<D>(kr, 2 * kc + g));
+}
+
+// A operand of Oᵀ = Vᵀ·Pᵀ for output columns 32db .. 32db+31 and the 16-key
+// chunk kc: lane l gets column 32db + l%32 at keys 16kc + 8(e/4) + 4g + e%4,
+// e = 0..7 (the Pᵀ key order), from two ds_read_b64_tr_b16. Within each
+// 16-lane group that instruction returns, to lane i, element i%4 of the
+// 8-byte reads of lanes i/4, i/4+4, i/4+8, i/4+12; so lane s of the group
+// points at row 4(s/4)-block, columns 4(s%4) .. +3.
+template <int D>
+__device__ __forceinline__ bf16x8 vt_frag(const __bf16 *Vs, int db, int kc, int lane) {
+    const int G = lane >> 4, i16 = lane & 15, g = lane >> 5;
+    i16x4 half[2];
+#pragma unroll
+    for (int hr = 0; hr < 2; ++hr) {
+        const int vr = 16 * kc + 8 * hr + 4 * g + (i16 >> 2);
+        const int col = 32 * db + 16 * (G & 1) + 4 * (i16 & 3);
+        const __bf16 *src = Vs + vr * D + 8 * v_chunk<D>(vr, col >> 3) + (col & 7);
+        half[hr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4 *)(src));
+    }
+    const i16x8 v8 = __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v8);
 }
 
 }  // namespace attn

@@ -1,6 +1,7 @@
 // Probes of the tile layer, one wave each, for the GPU unit tests: the MFMA
-// fragment layout, the cross-half wave reductions, the Vᵀ key order used by
-// the P·V contraction, and the lane layout of the LDS transpose read. They
+// fragment layout, the cross-half wave reductions, the swizzled K fragment
+// path of Q·Kᵀ, the transposed V fragment path of P·V, and the lane layout of
+// the LDS transpose read. They
 // check the primitives the attention kernel is built from, separately from it
 // ("Distilling a 4.5 hour CUDA talk", section 9: unit tests over every
 // load/store/layout/MMA combination).
@@ -32,45 +33,58 @@ __global__ void __launch_bounds__(64) xhalf_probe(const float *x, float *mx, flo
     sm[lane] = xhalf_sum(x[lane]);
 }
 
-// Pᵀ·V through the kernel's own path: scores Sᵀ (32 keys x 32 queries,
-// supplied already in accumulator layout by the host as a row-major 32x32
-// matrix), converted to bf16 Pᵀ operands, times V (32 keys x 32 columns,
-// row-major bf16) staged to LDS in the permuted Vᵀ order. Output O is 32
-// queries x 32 columns, row-major fp32.
-__global__ void __launch_bounds__(64) pv_probe(const float *St, const __bf16 *Vg, float *O) {
-    constexpr int PV = 32 + 8;
-    __shared__ __attribute__((aligned(16))) __bf16 vt[32 * PV];
+// Sᵀ = K·Qᵀ through the kernel's fragment path: K (32 keys x D, row-major
+// bf16) is written to LDS in the swizzled K layout, Q (32 rows x D) is read
+// into B fragments as the kernel does. St is 32 keys x 32 queries, fp32.
+template <int D>
+__global__ void __launch_bounds__(64) qk_probe(const __bf16 *Kg, const __bf16 *Qg, float *St) {
+    __shared__ __attribute__((aligned(16))) __bf16 ks[32 * D];
     const int lane = threadIdx.x, l32 = lane & 31, g = lane >> 5;
-    // stage: lanes 0..31 each handle keys 4*(lane%8) .. +3, columns 8*(lane/8) .. +7
-    if (lane < 32) {
-        const int kq = lane % 8, d8 = lane / 8;
-        u32x4 vr[4];
-        for (int j = 0; j < 4; ++j) vr[j] = *(const u32x4 *)(Vg + (4 * kq + j) * 32 + 8 * d8);
-        const int pos = vt_pos(4 * kq);
-        for (int i = 0; i < 8; ++i) {
-            const int p = i >> 1;
-            const bool hi = i & 1;
-            *(u32x2 *)(vt + (8 * d8 + i) * PV + pos) =
-                u32x2{pick_halves(vr[0][p], vr[1][p], hi), pick_halves(vr[2][p], vr[3][p], hi)};
-        }
+    for (int ch = lane; ch < 32 * D / 8; ch += 64) {
+        const int r = ch / (D / 8), c = ch % (D / 8);
+        *(u32x4 *)(ks + r * D + 8 * k_chunk<D>(r, c)) = *(const u32x4 *)(Kg + r * D + 8 * c);
     }
     __syncthreads();
     f32x16 s;
-    for (int r = 0; r < 16; ++r) s[r] = St[acc_row(r, g) * 32 + l32];
-    bf16x8 pf[2];
-    for (int hh = 0; hh < 2; ++hh) {
-        u32x4 v;
-        for (int e = 0; e < 4; ++e) v[e] = pack_bf16x2(s[8 * hh + 2 * e], s[8 * hh + 2 * e + 1]);
-        pf[hh] = u32x4_as_bf16x8(v);
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+    for (int kc = 0; kc < D / 16; ++kc) {
+        const bf16x8 qf = u32x4_as_bf16x8(*(const u32x4 *)(Qg + l32 * D + 16 * kc + 8 * g));
+        s = mfma_32x32x16(k_frag<D>(ks, l32, kc, g), qf, s);
     }
-    f32x16 o;
-    for (int r = 0; r < 16; ++r) o[r] = 0.f;
-    for (int kc = 0; kc < 2; ++kc) {
-        const bf16x8 vf = *(const bf16x8 *)(vt + l32 * PV + 16 * kc + 8 * g);
-        o = mfma_32x32x16(vf, pf[kc], o);
+    for (int r = 0; r < 16; ++r) St[acc_row(r, g) * 32 + l32] = s[r];
+}
+
+// Oᵀ = Vᵀ·Pᵀ through the kernel's fragment path: scores St (64 keys x 32
+// queries, fp32) are taken in accumulator layout and packed to bf16 Pᵀ
+// operands as the kernel does; V (64 keys x D, row-major bf16) is written to
+// LDS in the swizzled V layout and read with transpose reads. O is
+// 32 queries x D, fp32.
+template <int D>
+__global__ void __launch_bounds__(64) pv_probe(const float *St, const __bf16 *Vg, float *O) {
+    __shared__ __attribute__((aligned(16))) __bf16 vs[64 * D];
+    const int lane = threadIdx.x, l32 = lane & 31, g = lane >> 5;
+    for (int ch = lane; ch < 64 * D / 8; ch += 64) {
+        const int r = ch / (D / 8), c = ch % (D / 8);
+        *(u32x4 *)(vs + r * D + 8 * v_chunk<D>(r, c)) = *(const u32x4 *)(Vg + r * D + 8 * c);
     }
-    // o holds Oᵀ: row = output column, column = query
-    for (int r = 0; r < 16; ++r) O[l32 * 32 + acc_row(r, g)] = o[r];
+    __syncthreads();
+    bf16x8 pf[4];
+    for (int kb = 0; kb < 2; ++kb)
+        for (int hh = 0; hh < 2; ++hh) {
+            u32x4 v;
+            for (int e = 0; e < 4; ++e) {
+                const float lo = St[(32 * kb + acc_row(8 * hh + 2 * e, g)) * 32 + l32];
+                const float hi = St[(32 * kb + acc_row(8 * hh + 2 * e + 1, g)) * 32 + l32];
+                v[e] = pack_bf16x2(lo, hi);
+            }
+            pf[2 * kb + hh] = u32x4_as_bf16x8(v);
+        }
+    for (int db = 0; db < D / 32; ++db) {
+        f32x16 o;
+        for (int r = 0; r < 16; ++r) o[r] = 0.f;
+        for (int kc = 0; kc < 4; ++kc) o = mfma_32x32x16(vt_frag<D>(vs, db, kc, lane), pf[kc], o);
+        for (int r = 0; r < 16; ++r) O[l32 * D + 32 * db + acc_row(r, g)] = o[r];
+    }
 }
 
 // ds_read_b64_tr_b16: LDS holds n 16-bit values equal to their index; lane l
@@ -102,9 +116,27 @@ int tile_selftest_xhalf(const void *x, void *mx, void *sm, void *stream) {
     return (int)hipGetLastError();
 }
 
-int tile_selftest_pv(const void *St, const void *V, void *O, void *stream) {
-    hipLaunchKernelGGL(pv_probe, dim3(1), dim3(64), 0, (hipStream_t)stream, (const float *)St,
-                       (const __bf16 *)V, (float *)O);
+int tile_selftest_qk(int d, const void *K, const void *Q, void *St, void *stream) {
+    if (d == 64)
+        hipLaunchKernelGGL(qk_probe<64>, dim3(1), dim3(64), 0, (hipStream_t)stream,
+                           (const __bf16 *)K, (const __bf16 *)Q, (float *)St);
+    else if (d == 128)
+        hipLaunchKernelGGL(qk_probe<128>, dim3(1), dim3(64), 0, (hipStream_t)stream,
+                           (const __bf16 *)K, (const __bf16 *)Q, (float *)St);
+    else
+        return -1;
+    return (int)hipGetLastError();
+}
+
+int tile_selftest_pv(int d, const void *St, const void *V, void *O, void *stream) {
+    if (d == 64)
+        hipLaunchKernelGGL(pv_probe<64>, dim3(1), dim3(64), 0, (hipStream_t)stream,
+                           (const float *)St, (const __bf16 *)V, (float *)O);
+    else if (d == 128)
+        hipLaunchKernelGGL(pv_probe<128>, dim3(1), dim3(64), 0, (hipStream_t)stream,
+                           (const float *)St, (const __bf16 *)V, (float *)O);
+    else
+        return -1;
     return (int)hipGetLastError();
 }
 

@@ -15,9 +15,12 @@ SELFTEST = os.path.join(ROOT, "accelerator_programming_amd", "libattn_tile_selft
 @pytest.fixture(scope="module")
 def lib():
     L = ctypes.CDLL(SELFTEST)
-    for n in ("tile_selftest_mfma", "tile_selftest_xhalf", "tile_selftest_pv"):
+    for n in ("tile_selftest_mfma", "tile_selftest_xhalf"):
         getattr(L, n).restype = ctypes.c_int
         getattr(L, n).argtypes = [ctypes.c_void_p] * 4
+    for n in ("tile_selftest_qk", "tile_selftest_pv"):
+        getattr(L, n).restype = ctypes.c_int
+        getattr(L, n).argtypes = [ctypes.c_int] + [ctypes.c_void_p] * 4
     return L
 
 
@@ -52,13 +55,25 @@ def test_cross_half_max_and_sum(lib):
     assert torch.equal(sm.cpu(), x + other)
 
 
-def test_pv_through_permuted_vt(lib):
+@pytest.mark.parametrize("d", [64, 128])
+def test_qk_through_swizzled_k_tile(lib, d):
+    K = small_ints((32, d), 6, -2, 3)
+    Q = small_ints((32, d), 7, -2, 3)
+    St = torch.full((32, 32), float("nan"), device="cuda")
+    Kd, Qd = K.bfloat16().cuda(), Q.bfloat16().cuda()
+    assert lib.tile_selftest_qk(d, Kd.data_ptr(), Qd.data_ptr(), St.data_ptr(), stream()) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(St.cpu(), K @ Q.t())
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_pv_through_transposed_v_reads(lib, d):
     # St[key][query] in the accumulator layout; P = St^T rounded to bf16 (exact
     # here: quarter-integers), V small integers -> O = P·V exact in fp32.
-    St = small_ints((32, 32), 4) / 4
-    V = small_ints((32, 32), 5)
+    St = small_ints((64, 32), 4) / 4
+    V = small_ints((64, d), 5)
     Sd, Vd = St.cuda(), V.bfloat16().cuda()
-    O = torch.full((32, 32), float("nan"), device="cuda")
-    assert lib.tile_selftest_pv(Sd.data_ptr(), Vd.data_ptr(), O.data_ptr(), stream()) == 0
+    O = torch.full((32, d), float("nan"), device="cuda")
+    assert lib.tile_selftest_pv(d, Sd.data_ptr(), Vd.data_ptr(), O.data_ptr(), stream()) == 0
     torch.cuda.synchronize()
     assert torch.equal(O.cpu(), St.t() @ V)
