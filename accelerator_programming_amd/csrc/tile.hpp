@@ -128,4 +128,43 @@ __device__ __forceinline__ bf16x8 vt_frag(const __bf16 *Vs, int db, int kc, int 
     return __builtin_bit_cast(bf16x8, v8);
 }
 
+// LDS-DMA: 16 bytes from gptr (per lane) into LDS at lds_base + 16 * lane,
+// lds_base wave-uniform (it goes through M0). Issued as inline assembly so
+// that the compiler does not treat it as a store that every later LDS read
+// might alias (which would put a vmcnt(0) wait in front of those reads); the
+// caller owns the ordering: s_waitcnt vmcnt(0) and a barrier before any wave
+// reads the destination.
+// Nothing else in these kernels uses M0 (no LDS-size M0 on gfx9+, no
+// dynamic register indexing), so the assembly may set it freely.
+__device__ __forceinline__ void dma16_to_lds(const void *gptr, const void *lds_base) {
+    const uint32_t addr =
+        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)lds_base);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(addr), "v"(gptr)
+                 : "memory");
+}
+
+// Softmax work for one MFMA slot of the P·V / softmax overlap, as an
+// instruction group the compiler keeps in place (it is placed between two
+// MFMAs): the exponentials of NPAIR pairs of scores,
+//   p = 2^(s·c - m), ls += p, pk = bf16x2(p0, p1),
+// i.e. Map(exp) and Reduce(+) of the softmax. Every v_exp result is consumed
+// at least one instruction later (the transcendental forwarding hazard).
+__device__ __forceinline__ void exp_pair(float s0, float s1, float c, float negm, float &ls,
+                                         uint32_t &pk) {
+    float t0, t1;
+    asm volatile(
+        "v_fma_f32 %[t0], %[s0], %[c], %[nm]\n\t"
+        "v_fma_f32 %[t1], %[s1], %[c], %[nm]\n\t"
+        "v_exp_f32 %[t0], %[t0]\n\t"
+        "v_exp_f32 %[t1], %[t1]\n\t"
+        "v_add_f32 %[ls], %[ls], %[t0]\n\t"
+        "v_add_f32 %[ls], %[ls], %[t1]\n\t"
+        "v_cvt_pk_bf16_f32 %[pk], %[t0], %[t1]"
+        : [t0] "=&v"(t0), [t1] "=&v"(t1), [ls] "+v"(ls), [pk] "=v"(pk)
+        : [s0] "v"(s0), [s1] "v"(s1), [c] "s"(c), [nm] "v"(negm));
+}
+
+
 }  // namespace attn
