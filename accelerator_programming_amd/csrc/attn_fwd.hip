@@ -34,7 +34,7 @@ struct attn_fwd_plan {
 
 namespace {
 
-constexpr int64_t kMaxSlab = (int64_t)1 << 31;
+constexpr int64_t kMaxSlab = ((int64_t)1 << 31) - 1;
 
 bool fill_strides(int64_t s[3], int64_t H, int64_t N, int64_t d, int64_t row_min,
                   int64_t align_elems) {

@@ -5,44 +5,48 @@
 // disjoint-output-tile decomposition of "Distilling a 4.5 hour CUDA talk",
 // section 5. Inside it, the FlashAttention-2 structure of the same page's
 // section 7: the query tile stays in registers while K/V tiles stream through
-// on-chip memory (here a three-stage LDS ring), and the row softmax is carried
-// online with a running max m and normalizer l.
+// on-chip memory (LDS), and the row softmax is carried across key tiles with
+// a per-row reference and a normalizer.
 //
 // gfx950 mapping
-//  * 4 waves of 64 lanes, one per SIMD; wave w owns query rows
-//    q0 + 64w .. q0 + 64w + 63 as two 32-row blocks (rb = 0, 1). Every K or V
-//    fragment read from LDS feeds the MFMAs of both blocks, so a CU reads each
-//    tile four times per 256 rows and LDS bandwidth (about 128 bytes per
-//    clock per CU) stays well below what the MFMA pipe consumes.
+//  * 8 waves, two per SIMD. Waves p and p + 4 form a pair on SIMD p and share
+//    query rows q0 + 64p .. q0 + 64p + 63 (two 32-row blocks). In each 64-key
+//    tile, role r = 0 / 1 (wave p / p + 4) scores keys 32r .. 32r + 31 and
+//    accumulates O columns 64r .. 64r + 63 (d = 128; half of d in general).
+//    Every K or V fragment read from LDS feeds the MFMAs of both row blocks.
+//  * Why pairs: on gfx950 a wave's VALU work does not overlap its own MFMAs,
+//    while VALU and MFMA work of two waves on one SIMD do overlap. The two
+//    roles run their period in different orders (role 0: P·V, scores,
+//    softmax; role 1: scores, softmax, P·V), so each one's exponentials run
+//    while the other's MFMAs execute: compute never idle, as the pages ask
+//    ("CS149 L11: Programming Specialized Hardware", section 4, slide 35),
+//    with the producer / consumer split of "Distilling a 4.5 hour CUDA talk",
+//    section 12, becoming a score / value split between two waves.
 //  * Scores are computed transposed, Sᵀ = K·Qᵀ, with 32x32x16 bf16 MFMAs:
 //    A = a 32-key slab of K read from LDS, B = the block's Q fragment held in
-//    VGPRs for the whole loop. In the accumulator every lane then holds one
-//    query row (l % 32) and 16 keys, so the row max and row sum are in-lane,
-//    plus one swap with lane l ^ 32 for the max.
-//  * Oᵀ += Vᵀ·Pᵀ: Pᵀ is the score accumulator converted to bf16 in place.
-//    The keys a lane holds come in runs of four (rows 8*(r/4) + 4g + r%4), so
-//    the MFMA k index 8g + e names key 8*(e/4) + 4g + e%4 of each 16-key
-//    chunk. The Vᵀ operand is read from the row-major V tile with the LDS
-//    transpose read (ds_read_b64_tr_b16) in exactly that key order: P needs no
-//    data movement, V no transposing store. (The pages' P·V operand is
-//    likewise transposed at load time.)
+//    VGPRs for the whole loop. In the accumulator every lane holds one query
+//    row (l % 32) and 16 keys, so the softmax row work is in-lane.
+//  * Oᵀ += Vᵀ·Pᵀ: Pᵀ is the score accumulator converted to bf16 in place. The
+//    keys a lane holds come in runs of four (rows 8*(r/4) + 4g + r%4), so the
+//    MFMA k index 8g + e names key 8*(e/4) + 4g + e%4 of each 16-key chunk.
+//    The Vᵀ operand is read from the row-major V tile with the LDS transpose
+//    read (ds_read_b64_tr_b16) in exactly that key order. Each role writes its
+//    P to LDS in register order; both roles read both halves back.
 //  * Softmax in base 2 with log2(e) folded into the scale on the host, and
 //    one reciprocal per row at the end ("Distilling a 4.5 hour CUDA talk",
 //    section 2 on the base-2 exponential and on reciprocal reuse; section 7
 //    on folding log2(e) into the temperature). Each row's exponent reference
 //    m is fixed from its first 32 keys: O = acc / l and lse = m + log2 l are
-//    exact in real arithmetic for any m, so no rescaling happens inside the
-//    loop. If some row's l leaves [0, 2^32] (a later key outscored the first
-//    ones by a wide margin) the workgroup recomputes with exact row maxima.
-//  * Per 32-key sub-tile: the Sᵀ MFMAs, then the P·V MFMAs of the previous
-//    sub-tile with the exponentials of this one placed between them.
-//  * K/V staging: LDS-DMA (global_load_lds_dwordx4, no VGPRs) into a
-//    three-stage ring per tensor. In 64-key tile T the waves issue K(T+2) and
-//    V(T+1) and read K(T), K(T+1), V(T-1), V(T); "my loads landed"
-//    (s_waitcnt vmcnt(0)) plus one barrier per tile close the tile. LDS-DMA
-//    writes 16 bytes per lane at consecutive addresses, so bank-conflict
-//    avoidance is an XOR swizzle of the 16-byte chunks of a row, applied by
-//    choosing which global chunk each lane fetches.
+//    exact in real arithmetic for any m, so nothing is rescaled in the loop.
+//    If some row's l leaves [0, 2^32] (a later key outscored the first ones by
+//    a wide margin) the workgroup recomputes with exact row maxima.
+//  * K/V staging: role-1 waves are also the loaders: they issue LDS-DMA
+//    (global_load_lds_dwordx4, no VGPRs) for K(T+1) and V(T) at the start of
+//    period T into two-stage rings; "my loads landed" (s_waitcnt vmcnt(0))
+//    plus one barrier close each period. LDS-DMA writes 16 bytes per lane at
+//    consecutive addresses, so bank-conflict avoidance is an XOR swizzle of the
+//    16-byte chunks of a row, applied by choosing which global chunk each lane
+//    fetches ("Distilling a 4.5 hour CUDA talk", section 8).
 #pragma once
 #include <type_traits>
 
@@ -64,40 +68,43 @@ struct KernelArgs {
 template <int D>
 struct TileCfg {
     static constexpr int TQ = 256;          // query rows per workgroup
-    static constexpr int TK = 64;           // keys per LDS tile (two 32-key sub-tiles)
-    static constexpr int NWAVE = 4;
+    static constexpr int TK = 64;           // keys per tile (one 32-key half per role)
+    static constexpr int NWAVE = 8;
     static constexpr int NT = 64 * NWAVE;   // threads per workgroup
-    static constexpr int NSTAGE = 3;        // LDS ring depth for K and for V
     static constexpr int CPR = D / 8;       // 16-byte chunks per K or V row
     static constexpr int TILE = TK * D;     // elements of one K or V tile
-    static constexpr int LDS_ELEMS = 2 * NSTAGE * TILE;
-    static constexpr int LDS_BYTES = LDS_ELEMS * 2;
-    static constexpr int ROWS_PER_DMA = 64 / CPR;                   // rows per wave-wide DMA
-    static constexpr int DMA_PER_WAVE = TK / ROWS_PER_DMA / NWAVE;  // per tile per tensor
+    static constexpr int P_BYTES = 4096;    // one wave's P: 64 rows x 32 keys bf16
+    static constexpr int P_SLOT = NWAVE * P_BYTES;
+    static constexpr int KV_BYTES = 4 * TILE * 2;  // two K stages, two V stages
+    static constexpr int LDS_BYTES = KV_BYTES + 2 * P_SLOT;
+    static constexpr int ROWS_PER_DMA = 64 / CPR;                 // rows per wave-wide DMA
+    static constexpr int DMA_PER_LOADER = TK / ROWS_PER_DMA / 4;  // per tile, tensor and loader wave
     static constexpr int NKC = D / 16;      // k-steps of Sᵀ = K·Qᵀ
-    static constexpr int NDB = D / 32;      // 32-column blocks of O
-    static_assert(TK % (ROWS_PER_DMA * NWAVE) == 0, "tile rows must split over the waves");
+    static constexpr int NDB = D / 64;      // 32-column blocks of O per role
+    static_assert(TK % (ROWS_PER_DMA * 4) == 0, "tile rows must split over the loader waves");
+    static_assert(D % 64 == 0, "each role owns a multiple of 32 output columns");
 };
 
-// Two 32-row blocks x two 16-key chunks of bf16 Pᵀ operands.
-struct PTile {
-    bf16x8 v[2][2];
-};
+template <int N>
+using IC = std::integral_constant<int, N>;
 
 template <int D, bool CAUSAL, typename TIn>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_kernel(const KernelArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
     using C = TileCfg<D>;
     constexpr int TQ = C::TQ, TK = C::TK, CPR = C::CPR, NKC = C::NKC, NDB = C::NDB;
-    __shared__ __attribute__((aligned(1024))) __bf16 lds[C::LDS_ELEMS];
-    __bf16 *const Kst = lds;                        // K stages
-    __bf16 *const Vst = lds + C::NSTAGE * C::TILE;  // V stages
+    constexpr int DPL = C::DMA_PER_LOADER;
+    __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[C::LDS_BYTES];
+    __bf16 *const Kst = (__bf16 *)lds_raw;             // two K stages
+    __bf16 *const Vst = Kst + 2 * C::TILE;             // two V stages
+    unsigned char *const Pst = lds_raw + C::KV_BYTES;  // two P slots
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
+    int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l32 = lane & 31, g = lane >> 5;
+    const int pair = w & 3, role = w >> 2;
+    int l32 = lane & 31, g = lane >> 5;
 
     // ---- work item: heaviest causal tiles are dispatched first -------------
     const int BH = a.B * a.Hq;
@@ -111,17 +118,19 @@ attn_fwd_kernel(const KernelArgs a) {
     TIn *__restrict__ Op = (TIn *)a.o + b * a.o_sb + h * a.o_sh;
 
     const int q0 = qt * TQ;
-    const int wrow0 = q0 + 64 * w;  // first query row of this wave
+    const int prow0 = q0 + 64 * pair;  // first query row of this pair
     const int kv_end = CAUSAL ? min(a.Nkv, q0 + TQ) : a.Nkv;
     const int n_tiles = (kv_end + TK - 1) / TK;  // >= 1
-    // 32-key sub-tiles from this index on need the causal or key-range mask
+    // 32-key half-tiles from this index on need the causal or key-range mask;
+    // tiles below n_plain have none
     const int first_masked_sub = CAUSAL ? min(q0 / 32, a.Nkv / 32) : a.Nkv / 32;
+    const int n_plain = min(n_tiles, first_masked_sub / 2);
 
     // ---- Q fragments: B operands of Sᵀ = K·Qᵀ, resident for the whole loop --
     bf16x8 qf[2][NKC];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-        const int row = wrow0 + 32 * rb + l32;
+        const int row = prow0 + 32 * rb + l32;
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc) {
             u32x4 v = {0, 0, 0, 0};
@@ -130,39 +139,65 @@ attn_fwd_kernel(const KernelArgs a) {
         }
     }
 
-    // ---- LDS-DMA of one K or V tile: each wave fills DMA_PER_WAVE windows
-    // of 64 lanes x 16 bytes; lane i of a window lands at chunk i. ----------
-    const int dma_r = lane / CPR;  // row within the window
-    const int dma_p = lane % CPR;  // physical chunk this lane fills
-    auto issue = [&](const TIn *base, int32_t sn, int tile, __bf16 *dst, bool is_v)
-                     __attribute__((always_inline)) {
+    // ---- LDS stages; PAR is the tile index parity (a compile-time constant
+    // in the unrolled loop, so stage offsets are instruction immediates) ----
+    auto kstage = [&](auto PAR) __attribute__((always_inline)) {
+        return Kst + decltype(PAR)::value * C::TILE;
+    };
+    auto vstage = [&](auto PAR) __attribute__((always_inline)) {
+        return Vst + decltype(PAR)::value * C::TILE;
+    };
+    // P of wave (pair, rl) for a tile of parity PAR, in register order:
+    // 16-byte chunk j of lane l at byte 16 * (64 j + l), conflict-free
+    auto pslot = [&](auto PAR, int rl) __attribute__((always_inline)) {
+        return Pst + decltype(PAR)::value * C::P_SLOT + (pair + 4 * rl) * C::P_BYTES;
+    };
+
+    // ---- LDS-DMA of one K or V tile by the four loader (role-1) waves. A
+    // window is 64 lanes x 16 bytes = ROWS_PER_DMA rows; loader `pair` fills
+    // windows pair, pair + 4, ...; lane i of a window lands at chunk i and
+    // fetches the global chunk that the swizzle puts there. bf16 inputs go
+    // through a buffer resource that ends at the last key, so rows past the
+    // end read as zeros (finite, and masked). -----------------------------
+    int dma_r = lane / CPR;  // row within the window
+    int dma_p = lane % CPR;  // physical chunk this lane fills
+    auto issue = [&](auto PAR, bool is_v, int tile) __attribute__((always_inline)) {
+        __bf16 *dst = is_v ? vstage(PAR) : kstage(PAR);
+        const TIn *base = is_v ? Vp : Kp;
+        const int32_t sn = is_v ? a.v_sn : a.k_sn;
+        if constexpr (sizeof(TIn) == 2) {
+            const int rem = a.Nkv - tile * TK;  // keys left, >= 1
+            const uint32_t bytes = (uint32_t)(((int64_t)(rem - 1) * sn + D) * 2);
+            const u32x4 rsrc = buffer_rsrc(base + (int64_t)tile * TK * sn, bytes);
 #pragma unroll
-        for (int u = 0; u < C::DMA_PER_WAVE; ++u) {
-            const int r = (w * C::DMA_PER_WAVE + u) * C::ROWS_PER_DMA + dma_r;  // tile row
-            const int key = min(tile * TK + r, a.Nkv - 1);  // clamped: a finite, masked row
-            const int chunk = is_v ? v_chunk<D>(r, dma_p) : k_chunk<D>(r, dma_p);
-            const TIn *src = base + (int64_t)key * sn + 8 * chunk;
-            __bf16 *win = dst + (w * C::DMA_PER_WAVE + u) * 64 * 8;
-            if constexpr (sizeof(TIn) == 2) {
-                dma16_to_lds(src, win);
-            } else {
-                // fp32 inputs: round to bf16 in registers, same LDS placement
-                *(u32x4 *)(win + 8 * lane) = load8_bf16(src);
+            for (int u = 0; u < DPL; ++u) {
+                const int win_id = 4 * u + pair;
+                const int r = win_id * C::ROWS_PER_DMA + dma_r;  // tile row
+                const int chunk = is_v ? v_chunk<D>(r, dma_p) : k_chunk<D>(r, dma_p);
+                const int64_t off = ((int64_t)r * sn + 8 * chunk) * 2;
+                const uint32_t voff = off < (int64_t)bytes ? (uint32_t)off : 0xFFFFFFF0u;
+                dma16_buf_to_lds(rsrc, voff, dst + win_id * 64 * 8);
+            }
+        } else {
+            // fp32 inputs: rounded to bf16 in registers, same LDS placement
+#pragma unroll
+            for (int u = 0; u < DPL; ++u) {
+                const int win_id = 4 * u + pair;
+                const int r = win_id * C::ROWS_PER_DMA + dma_r;
+                const int key = min(tile * TK + r, a.Nkv - 1);  // clamped: a finite, masked row
+                const int chunk = is_v ? v_chunk<D>(r, dma_p) : k_chunk<D>(r, dma_p);
+                *(u32x4 *)(dst + win_id * 64 * 8 + 8 * lane) =
+                    load8_bf16(base + (int64_t)key * sn + 8 * chunk);
             }
         }
     };
-    // ring slots; tile indices are never negative here (callers pass T + NSTAGE - 1 for T - 1)
-    auto kstage = [&](int tile) __attribute__((always_inline)) { return Kst + (tile % C::NSTAGE) * C::TILE; };
-    auto vstage = [&](int tile) __attribute__((always_inline)) { return Vst + (tile % C::NSTAGE) * C::TILE; };
 
     // ---- state -------------------------------------------------------------
-    f32x16 oacc[2][NDB];
-    float m[2];  // per-row reference of the exponentials (base 2, score*c units)
-    float l[2];  // normalizer, partial over this lane's keys
-    PTile pA, pB;
+    f32x16 oacc[2][NDB];  // O columns 32 * (NDB * role + db) .. of both row blocks
+    float m[2] = {0.f, 0.f};  // per-row reference of the exponentials (score*c units)
+    float l[2];               // normalizer, partial over this wave's keys and lane half
 
-    // Sᵀ of one 32-key sub-tile (rows kq_row0.. of K stage Kq) for both row
-    // blocks: 2*NKC MFMAs in two independent chains sharing each K fragment.
+    // Sᵀ of one 32-key half-tile (rows kq_row0.. of K stage Kq), both row blocks
     auto scores = [&](f32x16 (&sacc)[2], const __bf16 *Kq, int kq_row0)
                       __attribute__((always_inline)) {
 #pragma unroll
@@ -182,17 +217,17 @@ attn_fwd_kernel(const KernelArgs a) {
             asm volatile("" ::);
         }
     };
-    // scores of sub-tile js as floats, with the causal / key-range mask
-    auto masked_scores = [&](auto masked, const f32x16 (&sacc)[2], float (&sv)[2][16], int js)
+    // scores of half-tile js as floats, with the causal / key-range mask
+    auto masked_scores = [&](bool masked, const f32x16 (&sacc)[2], float (&sv)[2][16], int js)
                              __attribute__((always_inline)) {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) sv[rb][r] = sacc[rb][r];
-        if (decltype(masked)::value) {
+        if (masked) {
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
-                const int row = wrow0 + 32 * rb + l32;
+                const int row = prow0 + 32 * rb + l32;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = 32 * js + acc_row(r, g);
@@ -201,7 +236,7 @@ attn_fwd_kernel(const KernelArgs a) {
             }
         }
     };
-    // row maxima of score * c over a sub-tile (both wave halves)
+    // row maxima of score * c over a half-tile (both wave halves)
     auto row_max = [&](const float (&sv)[2][16], float (&mx)[2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
@@ -211,63 +246,72 @@ attn_fwd_kernel(const KernelArgs a) {
             mx[rb] = xhalf_max(x) * a.c;
         }
     };
-
-    // ---- one pipeline step (32-key sub-tile js) ----------------------------
-    // 1. Sᵀ(js) = K·Qᵀ.
-    // 2. Oᵀ += Vᵀ(js-1)·Pᵀ(js-1) (pin, V chunks pv_kc0.. of stage Vs) on the
-    //    MFMA pipe, issued slot by slot together with the exponentials of S(js)
-    //    into pout: p = 2^(s·c - m), with m the row's fixed reference.
-    // set_m: this is the first sub-tile of the pass and fixes m from its max.
-    auto step = [&](auto masked, bool set_m, PTile &pout, const __bf16 *Kq, int kq_row0,
-                    const PTile &pin, const __bf16 *Vs, int pv_kc0, int js)
-                    __attribute__((always_inline)) {
+    // this wave's half of tile T: scores, p = 2^(s·c - m) (Map(exp)), the
+    // partial row sums (Reduce(+)), P to LDS
+    auto score_softmax = [&](auto ROLE, auto PAR, int T, bool masked) __attribute__((always_inline)) {
+        constexpr int R = decltype(ROLE)::value;
         f32x16 sacc[2];
-        scores(sacc, Kq, kq_row0);
+        scores(sacc, kstage(PAR), 32 * R);
         float sv[2][16];
-        masked_scores(masked, sacc, sv, js);
-        if (set_m) {
-            float mx[2];
-            row_max(sv, mx);
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb) m[rb] = (mx[rb] == -INFINITY) ? 0.f : mx[rb];
-        }
-        const float negm[2] = {-m[0], -m[1]};
-        float ls[2] = {0.f, 0.f};
-        constexpr int NFV = 2 * NDB;       // Vᵀ fragments, each feeding two MFMAs
-        constexpr int NSLOT = 2 * NFV;     // MFMAs
-        constexpr int PAIRS = 16 / NSLOT;  // score pairs per slot (1 for d=128, 2 for d=64)
+        masked_scores(masked, sacc, sv, 2 * T + R);
         uint32_t pk[2][8];
-        bf16x8 vf[NFV];
-        vf[0] = vt_frag<D>(Vs, 0, pv_kc0, lane);
-        vf[1] = vt_frag<D>(Vs, 1 % NDB, pv_kc0 + 1 / NDB, lane);
-#pragma unroll
-        for (int f = 0; f < NFV; ++f) {
-            if (f + 2 < NFV) vf[f + 2] = vt_frag<D>(Vs, (f + 2) % NDB, pv_kc0 + (f + 2) / NDB, lane);
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-                const int slot = 2 * f + rb;
-                oacc[rb][f % NDB] = mfma_32x32x16(vf[f], pin.v[rb][f / NDB], oacc[rb][f % NDB]);
-#pragma unroll
-                for (int q = 0; q < PAIRS; ++q) {
-                    const int pp = PAIRS * slot + q, srb = pp / 8, r = 2 * (pp % 8);
-                    exp_pair(sv[srb][r], sv[srb][r + 1], a.c, negm[srb], ls[srb], pk[srb][r / 2]);
-                }
-            }
-        }
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
+            const float negm = -m[rb];
+            float ls = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) exp_pair(sv[rb][r], sv[rb][r + 1], a.c, negm, ls, pk[rb][r / 2]);
+            l[rb] += ls;
+        }
+        unsigned char *dst = pslot(PAR, R);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh)
-                pout.v[rb][hh] = u32x4_as_bf16x8(
-                    u32x4{pk[rb][4 * hh], pk[rb][4 * hh + 1], pk[rb][4 * hh + 2], pk[rb][4 * hh + 3]});
-            l[rb] += ls[rb];
+                *(u32x4 *)(dst + 16 * (64 * (2 * rb + hh) + lane)) =
+                    u32x4{pk[rb][4 * hh], pk[rb][4 * hh + 1], pk[rb][4 * hh + 2], pk[rb][4 * hh + 3]};
+    };
+    // O (own columns) += P·V for the tile of parity PAR, P of both roles read
+    // back from LDS
+    auto pv = [&](auto ROLE, auto PAR) __attribute__((always_inline)) {
+        constexpr int R = decltype(ROLE)::value;
+        const __bf16 *Vs = vstage(PAR);
+        bf16x8 pf[2][4];  // [rb][16-key chunk of the tile]
+#pragma unroll
+        for (int rl = 0; rl < 2; ++rl) {
+            const unsigned char *src = pslot(PAR, rl);
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+                    pf[rb][2 * rl + hh] = *(const bf16x8 *)(src + 16 * (64 * (2 * rb + hh) + lane));
+        }
+        constexpr int NFV = 4 * NDB;  // Vᵀ fragments: 4 key chunks x NDB column blocks
+        bf16x8 vf[NFV];
+        vf[0] = vt_frag<D>(Vs, NDB * R + 0 % NDB, 0 / NDB, lane);
+        vf[1] = vt_frag<D>(Vs, NDB * R + 1 % NDB, 1 / NDB, lane);
+#pragma unroll
+        for (int f = 0; f < NFV; ++f) {
+            if (f + 2 < NFV) vf[f + 2] = vt_frag<D>(Vs, NDB * R + (f + 2) % NDB, (f + 2) / NDB, lane);
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+                oacc[rb][f % NDB] = mfma_32x32x16(vf[f], pf[rb][f / NDB], oacc[rb][f % NDB]);
+            asm volatile("" ::);
         }
     };
 
-    // ---- one pass over the keys: O, l for the current references m ----------
-    // With set_m_first, m is fixed from each row's first 32 keys; otherwise m
-    // must already hold the exact row maxima.
-    auto pass = [&](bool set_m_first) __attribute__((always_inline)) {
+    // ---- one pass over the keys: O, l for the references m ------------------
+    // With set_m, m is first fixed from each row's first 32 keys (both roles
+    // compute the same value); otherwise m already holds the exact row maxima.
+    // Period T: the loaders bring K(T+1) and V(T); role 0 runs P·V(T-1), then
+    // its half of tile T; role 1 its half of tile T, then P·V(T-1).
+    auto pass = [&](auto ROLE, bool set_m) __attribute__((always_inline)) {
+        constexpr int R = decltype(ROLE)::value;
+        // an opaque copy of the lane index: the per-lane LDS and global
+        // offsets derived from it are then computed inside this role's branch
+        // and are not hoisted above it, where both roles' sets would be live
+        const int saved[5] = {lane, l32, g, dma_r, dma_p};
+        asm volatile("" : "+v"(lane), "+v"(l32), "+v"(g), "+v"(dma_r), "+v"(dma_p));
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
             l[rb] = 0.f;
@@ -275,102 +319,118 @@ attn_fwd_kernel(const KernelArgs a) {
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) oacc[rb][db][r] = 0.f;
-            // P of "sub-tile -1": zero, so the first step's P·V adds nothing
-            // (it reads V(0), which holds finite values)
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) pB.v[rb][hh] = u32x4_as_bf16x8(u32x4{0, 0, 0, 0});
         }
-        // prologue: K(0), K(1), V(0) in flight
-        issue(Kp, a.k_sn, 0, kstage(0), false);
-        if (n_tiles > 1) issue(Kp, a.k_sn, 1, kstage(1), false);
-        issue(Vp, a.v_sn, 0, vstage(0), true);
-        __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's DMA landed
+        if (R == 1) issue(IC<0>{}, false, 0);
+        __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
         __syncthreads();
-        auto tile = [&](int T, auto masked) __attribute__((always_inline)) {
-            if (T + 2 < n_tiles) issue(Kp, a.k_sn, T + 2, kstage(T + 2), false);
-            if (T + 1 < n_tiles) issue(Vp, a.v_sn, T + 1, vstage(T + 1), true);
-            // sub-tile 2T: first half of K(T); P·V of sub-tile 2T-1 (second half
-            // of V(T-1)) with pB; exponentials into pA
-            const __bf16 *Vprev = T > 0 ? vstage(T + C::NSTAGE - 1) : vstage(0);
-            step(masked, set_m_first && T == 0, pA, kstage(T), 0, pB, Vprev, 2, 2 * T);
-            // sub-tile 2T+1: second half of K(T); P·V of sub-tile 2T (first half
-            // of V(T)) with pA; exponentials into pB
-            step(masked, false, pB, kstage(T), 32, pA, vstage(T), 0, 2 * T + 1);
-            __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's DMAs of K(T+2), V(T+1) landed
+        if (set_m) {
+            f32x16 sacc[2];
+            scores(sacc, kstage(IC<0>{}), 0);
+            float sv[2][16], mx[2];
+            masked_scores(0 >= first_masked_sub, sacc, sv, 0);
+            row_max(sv, mx);
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) m[rb] = (mx[rb] == -INFINITY) ? 0.f : mx[rb];
+        }
+        auto period = [&](auto PAR, int T) __attribute__((always_inline)) {
+            constexpr int P = decltype(PAR)::value;
+            const bool masked = T >= n_plain;
+            if constexpr (R == 0) {
+                if (T > 0) pv(ROLE, IC<P ^ 1>{});
+                score_softmax(ROLE, PAR, T, masked);
+            } else {
+                if (T + 1 < n_tiles) issue(IC<P ^ 1>{}, false, T + 1);
+                issue(PAR, true, T);
+                score_softmax(ROLE, PAR, T, masked);
+                if (T > 0) pv(ROLE, IC<P ^ 1>{});
+            }
+            __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's DMAs landed
             __syncthreads();
         };
-        // tiles whose keys all precede every row of the workgroup need no mask
-        const int n_plain = min(n_tiles, first_masked_sub / 2);
-        for (int T = 0; T < n_plain; ++T) tile(T, std::integral_constant<bool, false>{});
-        for (int T = n_plain; T < n_tiles; ++T) tile(T, std::integral_constant<bool, true>{});
-        // P·V of the last sub-tile
-        const __bf16 *Vl = vstage(n_tiles - 1);
+        for (int T = 0; T < n_tiles; T += 2) {
+            period(IC<0>{}, T);
+            if (T + 1 < n_tiles) period(IC<1>{}, T + 1);
+        }
+        if ((n_tiles - 1) & 1)
+            pv(ROLE, IC<1>{});
+        else
+            pv(ROLE, IC<0>{});
+        lane = saved[0], l32 = saved[1], g = saved[2], dma_r = saved[3], dma_p = saved[4];
+    };
+    // normalizer of each row = this lane's part + the other lane half + partner
+    __shared__ float l_share[C::NWAVE][2][32];
+    __shared__ int wave_bad[C::NWAVE];
+    float l_row[2];
+    auto combine_l = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int kc2 = 0; kc2 < 2; ++kc2)
+        for (int rb = 0; rb < 2; ++rb) {
+            l_row[rb] = xhalf_sum(l[rb]);
+            if (g == 0) l_share[w][rb][l32] = l_row[rb];
+        }
+        __syncthreads();
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const bf16x8 vf = vt_frag<D>(Vl, db, 2 + kc2, lane);
-#pragma unroll
-                for (int rb = 0; rb < 2; ++rb)
-                    oacc[rb][db] = mfma_32x32x16(vf, pB.v[rb][kc2], oacc[rb][db]);
-            }
+        for (int rb = 0; rb < 2; ++rb) l_row[rb] += l_share[w ^ 4][rb][l32];
     };
 
-    // ---- fast pass: reference m fixed by each row's first 32 keys ------------
-    // Exact in real arithmetic for any m (O = acc / l, lse = m + log2 l); it
-    // only has to stay in range: p <= 2^32 is guaranteed when l <= 2^32.
-    pass(true);
-    constexpr float kMaxL = 4294967296.0f;  // 2^32
-    bool bad = false;
+    // ---- fast pass with m fixed by each row's first 32 keys; if some row's
+    // normalizer leaves [0, 2^32] (every p <= 2^32 when it does not), the
+    // exact row maxima are found and the pass runs again (rare) -----------
+    constexpr float kMaxL = 4294967296.0f;
+    for (bool exact = false;; exact = true) {
+        if (role == 0)
+            pass(IC<0>{}, !exact);
+        else
+            pass(IC<1>{}, !exact);
+        combine_l();
+        if (exact) break;
+        bool bad = false;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) bad |= !(xhalf_sum(l[rb]) <= kMaxL);  // also catches inf/NaN
-    __shared__ int wave_bad[C::NWAVE];
-    if (lane == 0) wave_bad[w] = __builtin_amdgcn_ballot_w64(bad) != 0;
-    __syncthreads();
-    const bool wg_bad = wave_bad[0] | wave_bad[1] | wave_bad[2] | wave_bad[3];
-    if (wg_bad) {
-        // ---- slow pass (rare: a later key outscored a row's first keys by
-        // more than 2^32): exact row maxima first, then the pass again ------
+        for (int rb = 0; rb < 2; ++rb) bad |= !(l_row[rb] <= kMaxL);  // also catches inf and NaN
+        if (lane == 0) wave_bad[w] = __builtin_amdgcn_ballot_w64(bad) != 0;
+        __syncthreads();
+        bool wg_bad = false;
+#pragma unroll
+        for (int i = 0; i < C::NWAVE; ++i) wg_bad |= wave_bad[i] != 0;
+        if (!wg_bad) break;
         float M[2] = {-INFINITY, -INFINITY};
         for (int T = 0; T < n_tiles; ++T) {
-            issue(Kp, a.k_sn, T, kstage(0), false);
+            __syncthreads();  // the previous tile's K stage is no longer read
+            if (role == 1) issue(IC<0>{}, false, T);
             __builtin_amdgcn_s_waitcnt(0x3f70);
             __syncthreads();
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 f32x16 sacc[2];
-                scores(sacc, kstage(0), 32 * half);
+                scores(sacc, kstage(IC<0>{}), 32 * half);
                 float sv[2][16], mx[2];
-                masked_scores(std::integral_constant<bool, true>{}, sacc, sv, 2 * T + half);
+                masked_scores(true, sacc, sv, 2 * T + half);
                 row_max(sv, mx);
                 M[0] = fmaxf(M[0], mx[0]);
                 M[1] = fmaxf(M[1], mx[1]);
             }
-            __syncthreads();
         }
+        __syncthreads();  // K stage 0 and l_share are free again
         m[0] = (M[0] == -INFINITY) ? 0.f : M[0];
         m[1] = (M[1] == -INFINITY) ? 0.f : M[1];
-        pass(false);
     }
 
     // ---- O = Oᵀ / l (one reciprocal per row), logsumexp ---------------------
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-        const int row = wrow0 + 32 * rb + l32;
-        const float l_row = xhalf_sum(l[rb]);
-        const float inv_l = 1.0f / l_row;
+        const int row = prow0 + 32 * rb + l32;
+        const float inv_l = 1.0f / l_row[rb];
         if (row < a.Nq) {
             TIn *orow = Op + (int64_t)row * a.o_sn;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
-                    const int col = 32 * db + acc_row(4 * rr, g);
+                    const int col = 32 * (NDB * role + db) + acc_row(4 * rr, g);
                     store4(orow + col, oacc[rb][db][4 * rr] * inv_l, oacc[rb][db][4 * rr + 1] * inv_l,
                            oacc[rb][db][4 * rr + 2] * inv_l, oacc[rb][db][4 * rr + 3] * inv_l);
                 }
-            if (g == 0 && a.lse)
-                a.lse[((int64_t)b * a.Hq + h) * a.Nq + row] = (m[rb] + log2f(l_row)) * 0.69314718055994531f;
+            if (role == 0 && g == 0 && a.lse)
+                a.lse[((int64_t)b * a.Hq + h) * a.Nq + row] = (m[rb] + log2f(l_row[rb])) * 0.69314718055994531f;
         }
     }
 #endif

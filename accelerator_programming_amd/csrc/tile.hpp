@@ -145,6 +145,25 @@ __device__ __forceinline__ void dma16_to_lds(const void *gptr, const void *lds_b
                  : "memory");
 }
 
+// Raw buffer resource over [base, base + bytes): loads at byte offsets
+// >= bytes return zeros instead of touching memory (gfx9 range checking
+// applies to the VGPR offset; the SGPR offset is kept 0).
+__device__ __forceinline__ u32x4 buffer_rsrc(const void *base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    return u32x4{(uint32_t)a, (uint32_t)(a >> 32), bytes, 0x00020000u};
+}
+
+// The same LDS-DMA from a buffer resource: lane i fetches 16 bytes at byte
+// offset voff (zeros when out of range) into lds_base + 16 * i.
+__device__ __forceinline__ void dma16_buf_to_lds(u32x4 rsrc, uint32_t voff, const void *lds_base) {
+    const uint32_t addr =
+        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)lds_base);
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(addr), "v"(voff), "s"(rsrc)
+                 : "memory");
+}
+
 // Softmax work for one MFMA slot of the P·V / softmax overlap, as an
 // instruction group the compiler keeps in place (it is placed between two
 // MFMAs): the exponentials of NPAIR pairs of scores,
