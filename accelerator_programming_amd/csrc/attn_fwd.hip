@@ -10,9 +10,11 @@
 
 #include "../../include/attn_fwd.h"
 #include "attn_fwd_kernel.hpp"
+#include "attn_fwd_wide_kernel.hpp"
 
 using attn::KernelArgs;
 using attn::TileCfg;
+using attn::WideCfg;
 
 namespace {
 
@@ -20,6 +22,7 @@ enum Variant : int32_t {
     V_D64_BF16 = 0,
     V_D128_BF16 = 1,
     V_D64_FP32 = 2,
+    V_D576_BF16 = 3,  // d_qk = 576, d_v = 512
 };
 
 }  // namespace
@@ -76,11 +79,17 @@ attn_status validate(const attn_fwd_params *in, attn_fwd_plan *out) {
     if (p.d == 64 && p.d_v == 64 && p.dtype == ATTN_BF16) variant = V_D64_BF16;
     else if (p.d == 128 && p.d_v == 128 && p.dtype == ATTN_BF16) variant = V_D128_BF16;
     else if (p.d == 64 && p.d_v == 64 && p.dtype == ATTN_FP32) variant = V_D64_FP32;
+    else if (p.d == 576 && p.d_v == 512 && p.dtype == ATTN_BF16) variant = V_D576_BF16;
     else return ATTN_ERR_UNSUPPORTED;
 
     out->p = p;
     out->variant = variant;
-    if (variant == V_D128_BF16) {
+    if (variant == V_D576_BF16) {
+        out->tile_q = WideCfg<576, 512>::TQ;
+        out->tile_k = WideCfg<576, 512>::TK;
+        out->block = WideCfg<576, 512>::NT;
+        out->lds_bytes = WideCfg<576, 512>::LDS_BYTES;
+    } else if (variant == V_D128_BF16) {
         out->tile_q = TileCfg<128>::TQ;
         out->tile_k = TileCfg<128>::TK;
         out->block = TileCfg<128>::NT;
@@ -101,6 +110,13 @@ attn_status validate(const attn_fwd_params *in, attn_fwd_plan *out) {
 template <int D, bool CAUSAL, typename T>
 hipError_t launch(const attn_fwd_plan *pl, const KernelArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL((attn::attn_fwd_kernel<D, CAUSAL, T>), dim3((uint32_t)pl->grid),
+                       dim3(pl->block), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <bool CAUSAL>
+hipError_t launch_wide(const attn_fwd_plan *pl, const KernelArgs &a, hipStream_t stream) {
+    hipLaunchKernelGGL((attn::attn_fwd_wide_kernel<576, 512, CAUSAL>), dim3((uint32_t)pl->grid),
                        dim3(pl->block), 0, stream, a);
     return hipGetLastError();
 }
@@ -183,6 +199,9 @@ attn_status attn_fwd_run(const attn_fwd_plan *plan, const void *Q, const void *K
             break;
         case V_D64_FP32:
             e = p.causal ? launch<64, true, float>(plan, a, s) : launch<64, false, float>(plan, a, s);
+            break;
+        case V_D576_BF16:
+            e = p.causal ? launch_wide<true>(plan, a, s) : launch_wide<false>(plan, a, s);
             break;
         default:
             return ATTN_ERR_INVALID;

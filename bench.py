@@ -40,6 +40,15 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
+def kernel_name(w):
+    """The kernel the library launches for workload w (as rocprofv3 names it)."""
+    causal = "true" if w.causal else "false"
+    if w.dqk == 576:
+        return "attn::attn_fwd_wide_kernel<576, 512, %s>" % causal
+    return "attn::attn_fwd_kernel<%d, %s, %s>" % (
+        w.dqk, causal, "__bf16" if w.dtype == torch.bfloat16 else "float")
+
+
 def traffic_for_current_kernel(workload_name: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None when it was taken on other kernel sources or another workload."""
@@ -171,9 +180,7 @@ def main() -> int:
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_for_current_kernel(w.name),
                      "kernel_ms_avg": round(kern_avg_ms, 4),
-                     "kernel": "attn::attn_fwd_kernel<%d, %s, %s>" % (
-                         w.dqk, "true" if w.causal else "false",
-                         "__bf16" if w.dtype == torch.bfloat16 else "float")},
+                     "kernel": kernel_name(w)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

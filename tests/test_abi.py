@@ -109,6 +109,13 @@ def ex_params(**kw):
     (dict(dtype=7), ATTN_ERR_INVALID),
     (dict(causal=1, N_kv=301), ATTN_ERR_INVALID),
     (dict(d_v=32), ATTN_ERR_UNSUPPORTED),
+    # the wide-head variant: d_qk 576 with d_v 512, bf16 only
+    (dict(d=576, d_v=512), ATTN_OK),
+    (dict(d=576, d_v=512, causal=1), ATTN_OK),
+    (dict(d=576, d_v=576), ATTN_ERR_UNSUPPORTED),
+    (dict(d=576, d_v=512, dtype=ATTN_FP32), ATTN_ERR_UNSUPPORTED),
+    # V as the first 512 columns of the 576-wide K rows
+    (dict(d=576, d_v=512, v_strides=(2 * 300 * 576, 300 * 576, 576)), ATTN_OK),
     # V as the first 64 columns of a 128-wide row: legal strides
     (dict(v_strides=(2 * 300 * 128, 300 * 128, 128)), ATTN_OK),
     # row stride smaller than the row
@@ -139,6 +146,18 @@ def test_plan_info_geometry():
     finally:
         attn.attn_fwd_destroy(plan)
     assert info["grid"] == 2 * 32 * (4096 // info["tile_q"])
+    assert info["block"] % 64 == 0
+    assert info["lds_bytes"] <= 160 * 1024
+
+
+def test_plan_info_geometry_wide_heads():
+    p = ex_params(B=1, H_q=128, H_kv=1, N=64, N_kv=8192, d=576, d_v=512, scale=1 / math.sqrt(576))
+    plan = attn.attn_fwd_create_ex(p)
+    try:
+        info = attn.attn_fwd_plan_info(plan)
+    finally:
+        attn.attn_fwd_destroy(plan)
+    assert info["grid"] == 128 * (64 // info["tile_q"])
     assert info["block"] % 64 == 0
     assert info["lds_bytes"] <= 160 * 1024
 

@@ -87,13 +87,32 @@ def test_c4_full_size_sampled():
     case(C4, rows=sample_rows(C4, 256))
 
 
+def test_c5_reduced_full():
+    # V a view of K's first 512 columns; 1000 keys = a ragged last tile
+    case(C5.with_(Hq=4, Nkv=1000))
+
+
 def test_c5_full_size_sampled():
-    try:
-        case(C5, rows=sample_rows(C5, 256))
-    except attn.AttnError as e:
-        if e.status == attn.ATTN_ERR_UNSUPPORTED:
-            pytest.skip("d_qk=576 / d_v=512 kernel variant not available in this build")
-        raise
+    case(C5, rows=sample_rows(C5, 256))
+
+
+# wide heads (d_qk 576, d_v 512) with their own V, causal, tiny and ragged
+WIDE = [
+    # B, Hq, Hkv, Nq, Nkv, causal, v_from_k
+    (1, 2, 1, 1, 1, False, True),
+    (1, 2, 2, 45, 45, True, False),
+    (2, 3, 1, 100, 100, True, True),
+    (1, 2, 1, 33, 257, False, False),
+]
+
+
+@pytest.mark.parametrize("shape", WIDE, ids=lambda s: "B%d_Hq%d_Hkv%d_Nq%d_Nkv%d_%s_%s" % (
+    s[0], s[1], s[2], s[3], s[4], "causal" if s[5] else "full", "vk" if s[6] else "v"))
+def test_wide_head_shapes(shape):
+    B, Hq, Hkv, Nq, Nkv, causal, vk = shape
+    w = Workload("wide", B, Hq, Hkv, Nq, Nkv, 576, 512, causal, torch.bfloat16, 31 + Nq + Nkv,
+                 v_from_k=vk)
+    case(w)
 
 
 # ---------------------------------------------------------------------------
