@@ -46,7 +46,7 @@ def kernel_name(w):
     if w.dqk == 576:
         return "attn::attn_fwd_wide_kernel<576, 512, %s>" % causal
     return "attn::attn_fwd_kernel<%d, %s, %s>" % (
-        w.dqk, causal, "__bf16" if w.dtype == torch.bfloat16 else "float")
+        w.dqk, causal, "__bf16" if str(w.dtype) == "torch.bfloat16" else "float")
 
 
 def traffic_for_current_kernel(workload_name: str):
@@ -107,6 +107,9 @@ def main() -> int:
     ap.add_argument("--config", default="C4", help="workload C1..C5 (the metric is quoted on C4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of attention: copy a MIB-MiB buffer 3 times (a reference "
+                         "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -115,6 +118,17 @@ def main() -> int:
         return 2
 
     import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": 4 * n, "bytes_written": 4 * n,
+                          "launches": 3}), flush=True)
+        return 0
 
     from accelerator_programming_amd import attn
     from accelerator_programming_amd.inputs import WORKLOADS, make_inputs
