@@ -254,14 +254,22 @@ attn_fwd_kernel(const KernelArgs a) {
         scores(sacc, kstage(PAR), 32 * R);
         float sv[2][16];
         masked_scores(masked, sacc, sv, 2 * T + R);
+        // p = 2^(s·c - m) rounded to bf16; the row sums add the rounded p
+        // (what P·V multiplies) two at a time with v_dot2_f32_bf16, in
+        // independent partial sums so no instruction waits on the previous
         uint32_t pk[2][8];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
             const float negm = -m[rb];
-            float ls = 0.f;
+            float e[16];
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) exp_pair(sv[rb][r], sv[rb][r + 1], a.c, negm, ls, pk[rb][r / 2]);
-            l[rb] += ls;
+            for (int r = 0; r < 16; ++r) e[r] = exp2_hw(__builtin_fmaf(sv[rb][r], a.c, negm));
+#pragma unroll
+            for (int j = 0; j < 8; ++j) pk[rb][j] = pack_bf16x2(e[2 * j], e[2 * j + 1]);
+            float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) ls[j & 3] = sum_bf16x2(pk[rb][j], ls[j & 3]);
+            l[rb] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
         }
         unsigned char *dst = pslot(PAR, R);
 #pragma unroll

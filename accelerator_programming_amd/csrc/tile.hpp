@@ -55,6 +55,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
+// acc + lo + hi of a packed bf16 pair, in fp32 (one v_dot2_f32_bf16 with 1, 1).
+__device__ __forceinline__ float sum_bf16x2(uint32_t pair, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
+}
+
 __device__ __forceinline__ bf16x8 u32x4_as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // Eight consecutive elements starting at p, as bf16 (16 bytes). fp32 inputs
@@ -106,6 +112,12 @@ __device__ __forceinline__ bf16x8 k_frag(const __bf16 *Ks, int kr, int kc, int g
     return *(const bf16x8 *)(Ks + kr * D + 8 * k_chunk<D>(kr, 2 * kc + g));
 }
 
+// Where k_frag(Ks, kr, 0, g) reads: the first 16 bytes of that fragment.
+template <int D>
+__device__ __forceinline__ const __bf16 &k_frag_ptr(const __bf16 *Ks, int kr, int g) {
+    return Ks[kr * D + 8 * k_chunk<D>(kr, g)];
+}
+
 // A operand of Oᵀ = Vᵀ·Pᵀ for output columns 32db .. 32db+31 and the 16-key
 // chunk kc: lane l gets column 32db + l%32 at keys 16kc + 8(e/4) + 4g + e%4,
 // e = 0..7 (the Pᵀ key order), from two ds_read_b64_tr_b16. Within each
@@ -128,6 +140,15 @@ __device__ __forceinline__ bf16x8 vt_frag(const __bf16 *Vs, int db, int kc, int 
     return __builtin_bit_cast(bf16x8, v8);
 }
 
+// Where the first of vt_frag(Vs, db, 0, lane)'s transpose reads points.
+template <int D>
+__device__ __forceinline__ const __bf16 *vt_read_ptr(const __bf16 *Vs, int db, int lane) {
+    const int G = lane >> 4, i16 = lane & 15, g = lane >> 5;
+    const int vr = 4 * g + (i16 >> 2);
+    const int col = 32 * db + 16 * (G & 1) + 4 * (i16 & 3);
+    return Vs + vr * D + 8 * v_chunk<D>(vr, col >> 3) + (col & 7);
+}
+
 // LDS-DMA: 16 bytes from gptr (per lane) into LDS at lds_base + 16 * lane,
 // lds_base wave-uniform (it goes through M0). Issued as inline assembly so
 // that the compiler does not treat it as a store that every later LDS read
@@ -143,6 +164,15 @@ __device__ __forceinline__ void dma16_to_lds(const void *gptr, const void *lds_b
                  :
                  : "s"(addr), "v"(gptr)
                  : "memory");
+}
+
+// The lane index, recomputed (v_mbcnt) at each call and opaque to the
+// compiler, so that values derived from it are formed where they are used
+// instead of being hoisted out of loops as long-lived registers.
+__device__ __forceinline__ int fresh_lane() {
+    int x;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(x));
+    return x;
 }
 
 // Raw buffer resource over [base, base + bytes): loads at byte offsets
