@@ -106,12 +106,32 @@ attn_fwd_kernel(const KernelArgs a) {
     const int pair = w & 3, role = w >> 2;
     int l32 = lane & 31, g = lane >> 5;
 
-    // ---- work item: heaviest causal tiles are dispatched first -------------
-    const int BH = a.B * a.Hq;
-    const int bh = blockIdx.x % BH;
-    int qt = blockIdx.x / BH;
-    if (CAUSAL) qt = a.n_qtiles - 1 - qt;
-    const int b = bh / a.Hq, h = bh % a.Hq, hk = h / a.group;
+    // ---- work item: heaviest causal tiles are dispatched first. Workgroups
+    // go to the 8 XCDs round-robin by index; when the kv-head groups split
+    // evenly over them, each XCD takes whole groups and runs the query heads
+    // of a group on the same q-tile side by side, so they read the same K/V
+    // tiles through that XCD's L2. ------------------------------------------
+    int b, h, qt;
+    {
+        const int n_groups = a.B * a.Hkv;
+        const int bid = blockIdx.x;
+        if (n_groups % 8 == 0) {
+            const int xcd = bid % 8, idx = bid / 8;
+            const int per_round = (n_groups / 8) * a.group;  // WGs of one q-tile on one XCD
+            const int qt_rank = idx / per_round, r = idx % per_round;
+            const int grp = xcd + 8 * (r / a.group);
+            b = grp / a.Hkv;
+            h = (grp % a.Hkv) * a.group + r % a.group;
+            qt = qt_rank;
+        } else {
+            const int BH = a.B * a.Hq;
+            b = (bid % BH) / a.Hq;
+            h = (bid % BH) % a.Hq;
+            qt = bid / BH;
+        }
+        if (CAUSAL) qt = a.n_qtiles - 1 - qt;
+    }
+    const int hk = h / a.group;
     const TIn *__restrict__ Qp = (const TIn *)a.q + b * a.q_sb + h * a.q_sh;
     const TIn *__restrict__ Kp = (const TIn *)a.k + b * a.k_sb + hk * a.k_sh;
     const TIn *__restrict__ Vp = (const TIn *)a.v + b * a.v_sb + hk * a.v_sh;
