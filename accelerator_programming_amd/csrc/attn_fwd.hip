@@ -11,6 +11,7 @@
 #include "../../include/attn_fwd.h"
 #include "attn_fwd_kernel.hpp"
 #include "attn_fwd_wide_kernel.hpp"
+#include "attn_fwd_wide_vk_kernel.hpp"
 
 using attn::KernelArgs;
 using attn::TileCfg;
@@ -114,10 +115,20 @@ hipError_t launch(const attn_fwd_plan *pl, const KernelArgs &a, hipStream_t stre
     return hipGetLastError();
 }
 
+// Wide heads: V given as the first d_v columns of K's rows takes the kernel
+// that stages only K; any other V takes the general one. Both use 32-row
+// tiles and 256 threads.
 template <bool CAUSAL>
 hipError_t launch_wide(const attn_fwd_plan *pl, const KernelArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL((attn::attn_fwd_wide_kernel<576, 512, CAUSAL>), dim3((uint32_t)pl->grid),
-                       dim3(pl->block), 0, stream, a);
+    static_assert(attn::WideVkCfg<576, 512>::TQ == WideCfg<576, 512>::TQ &&
+                      attn::WideVkCfg<576, 512>::NT == WideCfg<576, 512>::NT,
+                  "one grid for both wide kernels");
+    if (a.v_in_k)
+        hipLaunchKernelGGL((attn::attn_fwd_wide_vk_kernel<576, 512, CAUSAL>), dim3((uint32_t)pl->grid),
+                           dim3(pl->block), 0, stream, a);
+    else
+        hipLaunchKernelGGL((attn::attn_fwd_wide_kernel<576, 512, CAUSAL>), dim3((uint32_t)pl->grid),
+                           dim3(pl->block), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -187,6 +198,8 @@ attn_status attn_fwd_run(const attn_fwd_plan *plan, const void *Q, const void *K
     a.group = (int32_t)(p.H_q / p.H_kv);
     a.n_qtiles = (int32_t)plan->n_qtiles;
     a.c = plan->c;
+    a.v_in_k = (V == K && p.v_strides[0] == p.k_strides[0] && p.v_strides[1] == p.k_strides[1] &&
+                p.v_strides[2] == p.k_strides[2]) ? 1 : 0;
 
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;

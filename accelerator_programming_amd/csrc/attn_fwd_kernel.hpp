@@ -62,7 +62,8 @@ struct KernelArgs {
     int32_t q_sn, k_sn, v_sn, o_sn;                          // row strides (elements)
     int32_t B, Hq, Hkv, Nq, Nkv, group;                      // group = Hq / Hkv
     int32_t n_qtiles;
-    float c;  // softmax scale * log2(e)
+    float c;         // softmax scale * log2(e)
+    int32_t v_in_k;  // V is the first d_v columns of K's rows (same pointer and strides)
 };
 
 template <int D>
