@@ -30,6 +30,14 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(const bf16x8 a, const bf16x8 b, 
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// C += A·B on one 16x16x32 bf16 tile, fp32 accumulate. Lane l, quarter
+// G = l / 16: A = 8 bf16 of row (l % 16), k = 8G .. 8G+7; B = 8 bf16 of
+// column (l % 16), the same k range; C (4 fp32) = column (l % 16), rows
+// 4G .. 4G+3.
+__device__ __forceinline__ f32x4 mfma_16x16x32(const bf16x8 a, const bf16x8 b, const f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 // Row of the 32x32 accumulator held in register r by a lane of half g.
 __device__ __forceinline__ constexpr int acc_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
 

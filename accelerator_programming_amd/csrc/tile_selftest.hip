@@ -27,6 +27,19 @@ __global__ void __launch_bounds__(64) mfma_probe(const __bf16 *A, const __bf16 *
     for (int r = 0; r < 16; ++r) Cm[acc_row(r, g) * 32 + l32] = c[r];
 }
 
+// C (16x16, row-major fp32) = A (16x32, row-major bf16) · B (32x16, row-major bf16)
+__global__ void __launch_bounds__(64) mfma16_probe(const __bf16 *A, const __bf16 *B, float *Cm) {
+    const int lane = threadIdx.x, l16 = lane & 15, G = lane >> 4;
+    bf16x8 a, b;
+    for (int e = 0; e < 8; ++e) {
+        a[e] = A[l16 * 32 + 8 * G + e];
+        b[e] = B[(8 * G + e) * 16 + l16];
+    }
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+    c = mfma_16x16x32(a, b, c);
+    for (int i = 0; i < 4; ++i) Cm[(4 * G + i) * 16 + l16] = c[i];
+}
+
 __global__ void __launch_bounds__(64) xhalf_probe(const float *x, float *mx, float *sm) {
     const int lane = threadIdx.x;
     mx[lane] = xhalf_max(x[lane]);
@@ -106,6 +119,12 @@ extern "C" {
 
 int tile_selftest_mfma(const void *A, const void *B, void *C, void *stream) {
     hipLaunchKernelGGL(mfma_probe, dim3(1), dim3(64), 0, (hipStream_t)stream, (const __bf16 *)A,
+                       (const __bf16 *)B, (float *)C);
+    return (int)hipGetLastError();
+}
+
+int tile_selftest_mfma16(const void *A, const void *B, void *C, void *stream) {
+    hipLaunchKernelGGL(mfma16_probe, dim3(1), dim3(64), 0, (hipStream_t)stream, (const __bf16 *)A,
                        (const __bf16 *)B, (float *)C);
     return (int)hipGetLastError();
 }

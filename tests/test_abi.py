@@ -37,7 +37,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_selftest_library_loads():
     L = ctypes.CDLL(SELFTEST)
-    for n in ("tile_selftest_mfma", "tile_selftest_xhalf", "tile_selftest_qk", "tile_selftest_pv",
+    for n in ("tile_selftest_mfma", "tile_selftest_mfma16", "tile_selftest_xhalf", "tile_selftest_qk",
+              "tile_selftest_pv",
               "tile_selftest_tr16"):
         assert hasattr(L, n)
 

@@ -15,7 +15,7 @@ SELFTEST = os.path.join(ROOT, "accelerator_programming_amd", "libattn_tile_selft
 @pytest.fixture(scope="module")
 def lib():
     L = ctypes.CDLL(SELFTEST)
-    for n in ("tile_selftest_mfma", "tile_selftest_xhalf"):
+    for n in ("tile_selftest_mfma", "tile_selftest_mfma16", "tile_selftest_xhalf"):
         getattr(L, n).restype = ctypes.c_int
         getattr(L, n).argtypes = [ctypes.c_void_p] * 4
     for n in ("tile_selftest_qk", "tile_selftest_pv"):
@@ -39,6 +39,16 @@ def test_mfma_32x32x16_fragment_layout(lib):
     Ad, Bd = A.bfloat16().cuda(), B.bfloat16().cuda()
     C = torch.full((32, 32), float("nan"), device="cuda")
     assert lib.tile_selftest_mfma(Ad.data_ptr(), Bd.data_ptr(), C.data_ptr(), stream()) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(C.cpu(), A @ B)
+
+
+def test_mfma_16x16x32_fragment_layout(lib):
+    A = small_ints((16, 32), 4)
+    B = small_ints((32, 16), 5)
+    Ad, Bd = A.bfloat16().cuda(), B.bfloat16().cuda()
+    C = torch.full((16, 16), float("nan"), device="cuda")
+    assert lib.tile_selftest_mfma16(Ad.data_ptr(), Bd.data_ptr(), C.data_ptr(), stream()) == 0
     torch.cuda.synchronize()
     assert torch.equal(C.cpu(), A @ B)
 
