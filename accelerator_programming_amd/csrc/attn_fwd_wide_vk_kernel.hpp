@@ -179,16 +179,24 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
 
     // ---- K staging: piece u of wave w is the 1 KB at (4u + w) KB of the tile;
     // lane i moves its 16-byte unit 64 (4u + w) + i, which holds the logical
-    // chunk the swizzle puts there. Rows past the last key repeat the last
-    // key (finite values, masked). -----------------------------------------
-    auto load_tile = [&](int T, u32x4 (&kr)[C::KWIN_W]) __attribute__((always_inline)) {
+    // chunk the swizzle puts there. The byte offsets inside a tile are the
+    // same for every tile; the loads go through a buffer resource that ends
+    // at the last key, so rows past it read as zeros (finite, masked). -----
+    uint32_t koff[C::KWIN_W];
 #pragma unroll
-        for (int u = 0; u < C::KWIN_W; ++u) {
-            const int p = (C::NWAVE * u + w) * 64 + lane;
-            const int r = p / C::KCH, c = wide_vk_chunk(r, p % C::KCH);
-            const int key = min(T * TK + r, a.Nkv - 1);
-            kr[u] = load8_bf16(Kp + (int64_t)key * a.k_sn + 8 * c);
-        }
+    for (int u = 0; u < C::KWIN_W; ++u) {
+        const int p = (C::NWAVE * u + w) * 64 + lane;
+        const int r = p / C::KCH, c = wide_vk_chunk(r, p % C::KCH);
+        koff[u] = (uint32_t)r * (uint32_t)a.k_sn * 2u + 16u * (uint32_t)c;
+    }
+    auto load_tile = [&](int T, u32x4 (&kr)[C::KWIN_W]) __attribute__((always_inline)) {
+        const int rem = a.Nkv - T * TK;  // keys left, >= 1
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(Kp + (int64_t)T * TK * a.k_sn), (short)0,
+            (int)(((int64_t)(rem - 1) * a.k_sn + DQK) * 2), 0x00020000);
+#pragma unroll
+        for (int u = 0; u < C::KWIN_W; ++u)
+            kr[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff[u], 0, 0));
     };
     auto store_tile = [&](int stage, const u32x4 (&kr)[C::KWIN_W]) __attribute__((always_inline)) {
         unsigned char *st = lds + stage * C::KTILE_B;
@@ -230,22 +238,38 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
     float l;        // normalizer of row srow over this lane's keys
     float *stat = (float *)(lds + C::SOFF);  // [kh][32] per-half row values, then m[32]
 
-    // Vᵀ fragment (32 value columns from 32 db, keys 16 kc .. 16 kc + 15):
-    // transposed reads of the K tile, whose rows begin with the values
-    auto vt_frag_k = [&](const __bf16 *Ks, int db, int kc) __attribute__((always_inline)) {
-        const int Gq = lane >> 4, i16 = lane & 15;
+    // ---- Vᵀ fragments (value columns 32 db .. 32 db + 31, keys 16 kc ..
+    // 16 kc + 15, db = 4w + i): two transposed reads (key halves hr) of the K
+    // tile, whose rows begin with the values. Lane (4 g + i16 / 4 + 8 hr + 16 kc,
+    // column 32 db + 16 (G % 2) + 4 (i16 % 4)) reads 4 values. The row's
+    // swizzle s does not depend on kc, and XOR-ing the chunk 4 db + x (x < 4)
+    // with s gives 4 (db ^ s/4) + (x ^ s%4): the address of (i, kc, hr) is
+    // vtb[hr][i % 2] + 128 (i / 2) + 16 rows (kc). -------------------------
+    static_assert(CBW == 4, "column blocks 4w + i, i < 4");
+    uint32_t vtb[2][2];
+    {
+        const int i16 = lane & 15;
+#pragma unroll
+        for (int hr = 0; hr < 2; ++hr)
+#pragma unroll
+            for (int ip = 0; ip < 2; ++ip) {
+                const int vr = 8 * hr + 4 * g + (i16 >> 2);
+                const int col = 32 * (CBW * w + ip) + 16 * (G & 1) + 4 * (i16 & 3);
+                vtb[hr][ip] = (uint32_t)(uintptr_t)(lds_void *)lds +
+                              (uint32_t)(vr * C::KROW_B + 16 * wide_vk_chunk(vr, col >> 3) + 2 * (col & 7));
+            }
+    }
+    auto vt_frag_k = [&](uint32_t stage_off, int i, int kc) __attribute__((always_inline)) {
         i16x4 hv[2];
 #pragma unroll
         for (int hr = 0; hr < 2; ++hr) {
-            const int vr = 16 * kc + 8 * hr + 4 * g + (i16 >> 2);
-            const int col = 32 * db + 16 * (Gq & 1) + 4 * (i16 & 3);
-            const __bf16 *src = Ks + vr * DQK + 8 * wide_vk_chunk(vr, col >> 3) + (col & 7);
-            hv[hr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(src));
+            const uint32_t addr = vtb[hr][i & 1] + stage_off + 128 * (i >> 1) + 16 * C::KROW_B * kc;
+            hv[hr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(uintptr_t)addr);
         }
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(hv[0], hv[1], 0, 1, 2, 3, 4, 5, 6, 7));
     };
     auto pv = [&](const unsigned char *pb, int stage) __attribute__((always_inline)) {
-        const __bf16 *Ks = (const __bf16 *)(lds + stage * C::KTILE_B);
+        const uint32_t stage_off = stage * C::KTILE_B;
         bf16x8 pf[2];
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) pf[kc] = *(const bf16x8 *)(pb + p_rd + 32 * kc);
@@ -253,7 +277,7 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-            for (int i = 0; i < CBW; ++i) vf[kc][i] = vt_frag_k(Ks, CBW * w + i, kc);
+            for (int i = 0; i < CBW; ++i) vf[kc][i] = vt_frag_k(stage_off, i, kc);
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
