@@ -149,6 +149,12 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
     const int l32 = lane & 31, g = lane >> 5;    // 32x32 fragments (P·V)
     const int l16 = lane & 15, G = lane >> 4;    // 16x16 fragments (scores)
     const int kh = w & 1, rh = w >> 1;           // this wave's score block
+    // k-group of this lane's 8 contraction elements in a k-step: quarter G
+    // takes group (G % 2) * 2 + G / 2, so that the two quarters whose LDS
+    // reads are served together (lanes i and i + 32) read chunks 4 ks + x and
+    // 4 ks + x + 1 (x even): with the row swizzle below the 16 lanes of such a
+    // pass then hit distinct banks. Q uses the same assignment.
+    const int kg = ((G & 1) << 1) | (G >> 1);
 
     // ---- work item ----------------------------------------------------------
     const int BH = a.B * a.Hq;
@@ -173,7 +179,7 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
 #pragma unroll
     for (int ks = 0; ks < C::NKS; ++ks) {
         u32x4 v = {0, 0, 0, 0};
-        if (srow < a.Nq) v = load8_bf16(Qp + (int64_t)srow * a.q_sn + 32 * ks + 8 * G);
+        if (srow < a.Nq) v = load8_bf16(Qp + (int64_t)srow * a.q_sn + 32 * ks + 8 * kg);
         qf[ks] = u32x4_as_bf16x8(v);
     }
 
@@ -209,14 +215,14 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     };
 
-    // ---- K fragment addresses: key row r = 16 kh + l16, chunk 4 ks + G. With
-    // s = the row's swizzle, (4 ks + G) ^ s = 4 (ks ^ s/4) + (G ^ s%4), and
+    // ---- K fragment addresses: key row r = 16 kh + l16, chunk 4 ks + kg. With
+    // s = the row's swizzle, (4 ks + kg) ^ s = 4 (ks ^ s/4) + (kg ^ s%4), and
     // s/4 < 2 only flips ks's low bit: fragment 2 j + b is at kb_b + 128 j. --
     uint32_t kb[2];
     {
         const int r = 16 * kh + l16;
         const int t = (r >> 1) & 7, s = t ^ ((t & 1) << 2);
-        const uint32_t base = (uint32_t)(uintptr_t)(lds_void *)lds + (uint32_t)(r * C::KROW_B + 16 * (G ^ (s & 3)));
+        const uint32_t base = (uint32_t)(uintptr_t)(lds_void *)lds + (uint32_t)(r * C::KROW_B + 16 * (kg ^ (s & 3)));
         kb[0] = base + 64 * (0 ^ (s >> 2));
         kb[1] = base + 64 * (1 ^ (s >> 2));
     }

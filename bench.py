@@ -26,7 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12  # 2516.6
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_C4_traffic.json")
+PROFILES = os.path.join(ROOT, "profiles")
 METRIC = "attention fwd TFLOP/s on 1 MI355X + % of bf16 MFMA peak (causal FLOPs /2)"
 
 
@@ -44,16 +44,17 @@ def kernel_name(w):
     """The kernel the library launches for workload w (as rocprofv3 names it)."""
     causal = "true" if w.causal else "false"
     if w.dqk == 576:
-        return "attn::attn_fwd_wide_kernel<576, 512, %s>" % causal
+        # V given as the leading columns of K takes the kernel that stages K only
+        return "attn::attn_fwd_wide_%skernel<576, 512, %s>" % ("vk_" if w.v_from_k else "", causal)
     return "attn::attn_fwd_kernel<%d, %s, %s>" % (
         w.dqk, causal, "__bf16" if str(w.dtype) == "torch.bfloat16" else "float")
 
 
-def traffic_for_current_kernel(workload_name: str):
+def traffic_for_current_kernel(workload_name: str, tag: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None when it was taken on other kernel sources or another workload."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(os.path.join(PROFILES, "attn_fwd_%s_traffic.json" % tag)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -192,7 +193,7 @@ def main() -> int:
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_for_current_kernel(w.name),
+                     "traffic": traffic_for_current_kernel(w.name, args.config),
                      "kernel_ms_avg": round(kern_avg_ms, 4),
                      "kernel": kernel_name(w)},
         "cpu_baseline": cpu,
