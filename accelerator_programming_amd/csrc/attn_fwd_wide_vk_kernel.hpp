@@ -319,11 +319,11 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
             for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
         __syncthreads();  // the ring, the P buffers and the statistics are free
         load_tile(0, kr0);
-        if (n_tiles > 1) load_tile(1, kr1);
+        load_tile(min(1, n_tiles - 1), kr1);
         store_tile(0, kr0);
-        if (n_tiles > 1) store_tile(1, kr1);
-        if (n_tiles > 2) load_tile(2, kr0);
-        if (n_tiles > 3) load_tile(3, kr1);
+        store_tile(1, kr1);
+        load_tile(min(2, n_tiles - 1), kr0);
+        load_tile(min(3, n_tiles - 1), kr1);
         lds_barrier();
         kreads(0);
 
@@ -366,21 +366,22 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
             // the last compiler-placed LDS wait of P·V (such a wait would also
             // wait for them), so they overlap the P·V MFMAs and the staging
             if (mode != 2) pv(pb, stage);
-            if (T + 1 < n_tiles) kreads(stage == 2 ? 0 : stage + 1);
-            if (T + 2 < n_tiles) {
-                store_tile(stage == 0 ? 2 : stage - 1, kr);
-                if (T + 4 < n_tiles) load_tile(T + 4, kr);
-            }
+            // The staging below is unconditional (past the last tile it
+            // rewrites a free stage and reloads the last tile), so the
+            // compiler's count of loads in flight stays exact: at the store
+            // only the other register set's 9 younger loads may be pending.
+            kreads(stage == 2 ? 0 : stage + 1);
+            store_tile(stage == 0 ? 2 : stage - 1, kr);
+            load_tile(min(T + 4, n_tiles - 1), kr);
         };
-        int stage = 0;
-        for (int T = 0; T < n_tiles; T += 2) {
+        int stage = 0, T = 0;
+        for (; T + 1 < n_tiles; T += 2) {
             tile(T, stage, kr0);
             stage = stage == 2 ? 0 : stage + 1;
-            if (T + 1 < n_tiles) {
-                tile(T + 1, stage, kr1);
-                stage = stage == 2 ? 0 : stage + 1;
-            }
+            tile(T + 1, stage, kr1);
+            stage = stage == 2 ? 0 : stage + 1;
         }
+        if (T < n_tiles) tile(T, stage, kr0);
         return M;
     };
 
