@@ -21,12 +21,11 @@
 //  * Row statistics: the reference m of a row (the maximum over the first 32
 //    keys) and, at the end, its normalizer l are the two key halves' values
 //    combined through LDS.
-//  * K tiles (32 keys x 1152 bytes) sit in a three-stage LDS ring, filled
-//    through registers: each wave loads its quarter of tile T + 4 after it has
-//    written tile T + 2, which leaves two tiles of time for the global loads.
-//    One barrier per tile: P of tile T is written to a double-buffered area
-//    before it and read after it; a stage is rewritten only after every wave
-//    has passed the next tile's barrier.
+//  * K tiles (32 keys x 1152 bytes) sit in a four-stage LDS ring, filled by
+//    LDS-DMA (buffer_load ... lds): after tile T's barrier each wave copies
+//    its quarter of tile T + 3, and tile T + 2's barrier waits for it, which
+//    leaves two tiles of time for the copies. One barrier per tile: P of
+//    tile T is written to a double-buffered area before it and read after it.
 //  * K rows are 72 16-byte chunks. Chunk c of row r is stored at
 //    c ^ s(r), s(r) = t ^ 4 (t & 1), t = (r / 2) % 8: the 16 rows of a
 //    fragment read (ds_read_b128) fall in 16 distinct bank groups, and so do
@@ -54,7 +53,7 @@ struct WideVkCfg {
     static constexpr int KCH = DQK / 8;  // 16-byte chunks per K row
     static constexpr int KROW_B = 2 * DQK;
     static constexpr int KTILE_B = TK * KROW_B;
-    static constexpr int NSTAGE = 3;
+    static constexpr int NSTAGE = 4;
     static constexpr int NKS = DQK / 32;           // k-steps of a 16x16 score block
     static constexpr int PROW_B = 2 * TK + 16;     // P row: 32 bf16 + 16 bytes of padding
     static constexpr int PBUF_B = TQ * PROW_B;     // one P buffer
@@ -186,7 +185,7 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
     // ---- K staging: piece u of wave w is the 1 KB at (4u + w) KB of the tile;
     // lane i moves its 16-byte unit 64 (4u + w) + i, which holds the logical
     // chunk the swizzle puts there. The byte offsets inside a tile are the
-    // same for every tile; the loads go through a buffer resource that ends
+    // same for every tile; the copies go through a buffer resource that ends
     // at the last key, so rows past it read as zeros (finite, masked). -----
     uint32_t koff[C::KWIN_W];
 #pragma unroll
@@ -195,24 +194,25 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
         const int r = p / C::KCH, c = wide_vk_chunk(r, p % C::KCH);
         koff[u] = (uint32_t)r * (uint32_t)a.k_sn * 2u + 16u * (uint32_t)c;
     }
-    auto load_tile = [&](int T, u32x4 (&kr)[C::KWIN_W]) __attribute__((always_inline)) {
+    // LDS-DMA of tile T into a stage: 9 buffer_load ... lds per wave, each
+    // 1 KB, counted by vmcnt (nothing else in the loop uses it).
+    auto dma_tile = [&](int T, int stage) __attribute__((always_inline)) {
         const int rem = a.Nkv - T * TK;  // keys left, >= 1
-        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(Kp + (int64_t)T * TK * a.k_sn), (short)0,
-            (int)(((int64_t)(rem - 1) * a.k_sn + DQK) * 2), 0x00020000);
-#pragma unroll
-        for (int u = 0; u < C::KWIN_W; ++u)
-            kr[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff[u], 0, 0));
-    };
-    auto store_tile = [&](int stage, const u32x4 (&kr)[C::KWIN_W]) __attribute__((always_inline)) {
+        const u32x4 rk = buffer_rsrc(Kp + (int64_t)T * TK * a.k_sn,
+                                     (uint32_t)(((int64_t)(rem - 1) * a.k_sn + DQK) * 2));
         unsigned char *st = lds + stage * C::KTILE_B;
 #pragma unroll
-        for (int u = 0; u < C::KWIN_W; ++u) *(u32x4 *)(st + (C::NWAVE * u + w) * 1024 + 16 * lane) = kr[u];
+        for (int u = 0; u < C::KWIN_W; ++u) dma16_buf_to_lds(rk, koff[u], st + (C::NWAVE * u + w) * 1024);
     };
     // this wave's LDS accesses are done, then every wave reaches this point;
-    // global loads stay in flight (also a compiler memory barrier)
+    // DMAs stay in flight (also a compiler memory barrier)
     auto lds_barrier = [&]() __attribute__((always_inline)) {
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    };
+    // the same, after this wave's DMAs but the newest tile's (9) have landed:
+    // each wave waits for its own share, the barrier covers all shares
+    auto dma_barrier = [&]() __attribute__((always_inline)) {
+        asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     };
 
     // ---- K fragment addresses: key row r = 16 kh + l16, chunk 4 ks + kg. With
@@ -309,7 +309,6 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
     // mode 0: reference from the first tile, then O and l;
     // mode 1: O and l for the given reference m;
     // mode 2: exact row maxima only (returned, combined over the halves)
-    u32x4 kr0[C::KWIN_W], kr1[C::KWIN_W];
     auto pass = [&](int mode) __attribute__((always_inline)) {
         float M = -INFINITY;
         l = 0.f;
@@ -318,20 +317,17 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
         __syncthreads();  // the ring, the P buffers and the statistics are free
-        load_tile(0, kr0);
-        load_tile(min(1, n_tiles - 1), kr1);
-        store_tile(0, kr0);
-        store_tile(1, kr1);
-        load_tile(min(2, n_tiles - 1), kr0);
-        load_tile(min(3, n_tiles - 1), kr1);
-        lds_barrier();
+        dma_tile(0, 0);
+        dma_tile(min(1, n_tiles - 1), 1);
+        dma_tile(min(2, n_tiles - 1), 2);
+        asm volatile("s_waitcnt vmcnt(18)\n\ts_barrier" ::: "memory");  // tile 0 landed
         kreads(0);
 
-        // tile T reads stage T % 3; at its end this wave writes tile T + 2
-        // (held in kr[T % 2]) into stage (T + 2) % 3, the stage of tile T - 1,
-        // which every wave finished before this tile's barrier, then loads
-        // tile T + 4 into the same registers
-        auto tile = [&](int T, int stage, u32x4 (&kr)[C::KWIN_W]) __attribute__((always_inline)) {
+        // tile T reads stage T % 4. After its barrier (every wave is done
+        // with tile T - 1) this wave copies tile T + 3 into stage (T + 3) % 4,
+        // the stage of tile T - 1; the barrier of tile T + 1 waits for the
+        // copies of tile T + 2, made two tiles earlier.
+        auto tile = [&](int T, int stage) __attribute__((always_inline)) {
             const f32x4 sacc = wide_vk_qk(qf);
             float sv[4];
 #pragma unroll
@@ -346,7 +342,7 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
             unsigned char *pb = lds + C::POFF + (T & 1) * C::PBUF_B;
             if (mode == 2) {
                 M = fmaxf(M, block_row_max(sv) * a.c);
-                lds_barrier();
+                dma_barrier();
             } else {
                 if (mode == 0 && T == 0) {
                     // reference: the row maximum over tile 0 (extra barrier,
@@ -360,28 +356,20 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
                 const uint32_t p01 = pack_bf16x2(e0, e1), p23 = pack_bf16x2(e2, e3);
                 l = sum_bf16x2(p23, sum_bf16x2(p01, l));
                 *(u32x2 *)(pb + p_wr) = u32x2{p01, p23};
-                lds_barrier();
+                dma_barrier();
             }
+            const int next = (stage + 1) & 3;
+            dma_tile(min(T + 3, n_tiles - 1), (stage + 3) & 3);
             // tile T + 1 was written before this barrier. Its K reads go after
             // the last compiler-placed LDS wait of P·V (such a wait would also
             // wait for them), so they overlap the P·V MFMAs and the staging
             if (mode != 2) pv(pb, stage);
-            // The staging below is unconditional (past the last tile it
-            // rewrites a free stage and reloads the last tile), so the
-            // compiler's count of loads in flight stays exact: at the store
-            // only the other register set's 9 younger loads may be pending.
-            kreads(stage == 2 ? 0 : stage + 1);
-            store_tile(stage == 0 ? 2 : stage - 1, kr);
-            load_tile(min(T + 4, n_tiles - 1), kr);
+            kreads(next);
         };
-        int stage = 0, T = 0;
-        for (; T + 1 < n_tiles; T += 2) {
-            tile(T, stage, kr0);
-            stage = stage == 2 ? 0 : stage + 1;
-            tile(T + 1, stage, kr1);
-            stage = stage == 2 ? 0 : stage + 1;
-        }
-        if (T < n_tiles) tile(T, stage, kr0);
+        // the copies are unconditional (past the last tile a free stage gets
+        // the last tile again), so every barrier's vmcnt(9) is exact
+        for (int T = 0; T < n_tiles; ++T) tile(T, T & 3);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no copy outlives the pass
         return M;
     };
 

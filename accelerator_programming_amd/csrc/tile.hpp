@@ -199,7 +199,7 @@ __device__ __forceinline__ void dma16_buf_to_lds(u32x4 rsrc, uint32_t voff, cons
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :
                  : "s"(addr), "v"(voff), "s"(rsrc)
-                 : "memory");
+                 : "memory", "m0");
 }
 
 // Softmax work for one MFMA slot of the P·V / softmax overlap, as an
