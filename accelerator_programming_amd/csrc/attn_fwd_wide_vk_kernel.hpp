@@ -30,11 +30,13 @@
 //    c ^ s(r), s(r) = t ^ 4 (t & 1), t = (r / 2) % 8: the 16 rows of a
 //    fragment read (ds_read_b128) fall in 16 distinct bank groups, and so do
 //    the 4 x 4 row/column pieces of a transposed Vᵀ read (ds_read_b64_tr_b16).
-//  * The 18 K fragment reads of a tile's scores are issued once the previous
-//    tile's P·V MFMAs are, into registers the compiler does not allocate
-//    (v184 .. v255), so their latency overlaps those MFMAs; the 18 MFMAs
-//    are one assembly block that waits for each read in turn. (Left to itself
-//    the compiler issues each read right before its MFMA.)
+//  * Software pipeline: after the barrier of tile T a wave issues the LDS
+//    reads of P·V(T) and the 18 K fragment reads of tile T + 1's scores (into
+//    registers the compiler does not allocate, v184 .. v255), then the score
+//    MFMAs of T + 1 (one assembly block that waits for each read in turn),
+//    then the P·V MFMAs of T, then P of T + 1 and the barrier. So the read
+//    latencies overlap MFMA work instead of following a barrier. (Left to
+//    itself the compiler issues each K read right before its MFMA.)
 //  * Softmax in base 2 with the per-row reference fixed by the first 32
 //    keys, exact O = acc / l and lse, and a slow pass with exact row maxima
 //    when some row's normalizer leaves [0, 2^32] (as in the main kernel).
@@ -274,16 +276,19 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
         }
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(hv[0], hv[1], 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    auto pv = [&](const unsigned char *pb, int stage) __attribute__((always_inline)) {
+    // P·V of a tile in two parts: the LDS reads (P and the Vᵀ fragments) and
+    // the MFMAs, so that the next tile's score block can go between them
+    auto pv_reads = [&](const unsigned char *pb, int stage, bf16x8 (&pf)[2], bf16x8 (&vf)[2][CBW])
+                        __attribute__((always_inline)) {
         const uint32_t stage_off = stage * C::KTILE_B;
-        bf16x8 pf[2];
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) pf[kc] = *(const bf16x8 *)(pb + p_rd + 32 * kc);
-        bf16x8 vf[2][CBW];
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
             for (int i = 0; i < CBW; ++i) vf[kc][i] = vt_frag_k(stage_off, i, kc);
+    };
+    auto pv_mma = [&](const bf16x8 (&pf)[2], const bf16x8 (&vf)[2][CBW]) __attribute__((always_inline)) {
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
@@ -304,72 +309,97 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
         const float v0 = stat[16 * rh + l16], v1 = stat[32 + 16 * rh + l16];
         return is_max ? fmaxf(v0, v1) : v0 + v1;
     };
+    // the score block of tile T (its K fragments already read), masked
+    auto scores = [&](int T, float (&sv)[4]) __attribute__((always_inline)) {
+        const f32x4 sacc = wide_vk_qk(qf);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[i] = sacc[i];
+        if (T >= first_masked) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = T * TK + 16 * kh + 4 * G + i;
+                if ((CAUSAL && key > srow) || key >= a.Nkv) sv[i] = -INFINITY;
+            }
+        }
+    };
+    // P of the block (bf16) into tile T's P buffer, and l
+    auto block_p = [&](int T, const float (&sv)[4]) __attribute__((always_inline)) {
+        const float negm = -m;
+        const float e0 = exp2_hw(fmaf(sv[0], a.c, negm)), e1 = exp2_hw(fmaf(sv[1], a.c, negm));
+        const float e2 = exp2_hw(fmaf(sv[2], a.c, negm)), e3 = exp2_hw(fmaf(sv[3], a.c, negm));
+        const uint32_t p01 = pack_bf16x2(e0, e1), p23 = pack_bf16x2(e2, e3);
+        l = sum_bf16x2(p23, sum_bf16x2(p01, l));
+        *(u32x2 *)(lds + C::POFF + (T & 1) * C::PBUF_B + p_wr) = u32x2{p01, p23};
+    };
+    // tiles 0, 1, 2 into stages 0, 1, 2; tile 0 landed everywhere; its K
+    // fragment reads issued
+    auto prologue = [&]() __attribute__((always_inline)) {
+        __syncthreads();  // the ring, the P buffers and the statistics are free
+        dma_tile(0, 0);
+        dma_tile(min(1, n_tiles - 1), 1);
+        dma_tile(min(2, n_tiles - 1), 2);
+        asm volatile("s_waitcnt vmcnt(18)\n\ts_barrier" ::: "memory");
+        kreads(0);
+    };
 
-    // ---- one pass over the keys ---------------------------------------------
-    // mode 0: reference from the first tile, then O and l;
-    // mode 1: O and l for the given reference m;
-    // mode 2: exact row maxima only (returned, combined over the halves)
-    auto pass = [&](int mode) __attribute__((always_inline)) {
-        float M = -INFINITY;
+    // ---- one pass over the keys: O and l (set_m: the reference from tile 0)
+    // Tile T's stage is T % 4. Software pipeline, one barrier per tile:
+    //   [P·V reads of T] [K reads of T + 1] [copy of T + 3] [scores of T + 1]
+    //   [P·V MFMAs of T] [P of T + 1] barrier
+    // The barrier that publishes P of T + 1 also waits for this wave's copy
+    // of tile T + 2 (two tiles old); the copy of T + 3 goes into the stage of
+    // tile T - 1, which every wave finished before the previous barrier. The
+    // copies are unconditional (past the last tile a free stage gets the last
+    // tile again), so every vmcnt(9) is exact.
+    auto pass = [&](bool set_m) __attribute__((always_inline)) {
         l = 0.f;
 #pragma unroll
         for (int i = 0; i < CBW; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
-        __syncthreads();  // the ring, the P buffers and the statistics are free
-        dma_tile(0, 0);
-        dma_tile(min(1, n_tiles - 1), 1);
-        dma_tile(min(2, n_tiles - 1), 2);
-        asm volatile("s_waitcnt vmcnt(18)\n\ts_barrier" ::: "memory");  // tile 0 landed
-        kreads(0);
-
-        // tile T reads stage T % 4. After its barrier (every wave is done
-        // with tile T - 1) this wave copies tile T + 3 into stage (T + 3) % 4,
-        // the stage of tile T - 1; the barrier of tile T + 1 waits for the
-        // copies of tile T + 2, made two tiles earlier.
-        auto tile = [&](int T, int stage) __attribute__((always_inline)) {
-            const f32x4 sacc = wide_vk_qk(qf);
+        prologue();
+        {
             float sv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sv[i] = sacc[i];
-            if (T >= first_masked) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int key = T * TK + 16 * kh + 4 * G + i;
-                    if ((CAUSAL && key > srow) || key >= a.Nkv) sv[i] = -INFINITY;
-                }
+            scores(0, sv);
+            if (set_m) {
+                // reference: the row maximum over tile 0 (an extra barrier,
+                // the same in every wave)
+                const float mx = combine_halves(block_row_max(sv), true) * a.c;
+                m = (mx == -INFINITY) ? 0.f : mx;
             }
-            unsigned char *pb = lds + C::POFF + (T & 1) * C::PBUF_B;
-            if (mode == 2) {
-                M = fmaxf(M, block_row_max(sv) * a.c);
-                dma_barrier();
-            } else {
-                if (mode == 0 && T == 0) {
-                    // reference: the row maximum over tile 0 (extra barrier,
-                    // the same in every wave)
-                    const float mx = combine_halves(block_row_max(sv), true) * a.c;
-                    m = (mx == -INFINITY) ? 0.f : mx;
-                }
-                const float negm = -m;
-                const float e0 = exp2_hw(fmaf(sv[0], a.c, negm)), e1 = exp2_hw(fmaf(sv[1], a.c, negm));
-                const float e2 = exp2_hw(fmaf(sv[2], a.c, negm)), e3 = exp2_hw(fmaf(sv[3], a.c, negm));
-                const uint32_t p01 = pack_bf16x2(e0, e1), p23 = pack_bf16x2(e2, e3);
-                l = sum_bf16x2(p23, sum_bf16x2(p01, l));
-                *(u32x2 *)(pb + p_wr) = u32x2{p01, p23};
+            block_p(0, sv);
+            dma_barrier();
+        }
+        for (int T = 0; T < n_tiles; ++T) {
+            const bool more = T + 1 < n_tiles;
+            bf16x8 pf[2], vf[2][CBW];
+            pv_reads(lds + C::POFF + (T & 1) * C::PBUF_B, T & 3, pf, vf);
+            if (more) kreads((T + 1) & 3);
+            dma_tile(min(T + 3, n_tiles - 1), (T + 3) & 3);
+            float sv[4];
+            if (more) scores(T + 1, sv);
+            pv_mma(pf, vf);
+            if (more) {
+                block_p(T + 1, sv);
                 dma_barrier();
             }
-            const int next = (stage + 1) & 3;
-            dma_tile(min(T + 3, n_tiles - 1), (stage + 3) & 3);
-            // tile T + 1 was written before this barrier. Its K reads go after
-            // the last compiler-placed LDS wait of P·V (such a wait would also
-            // wait for them), so they overlap the P·V MFMAs and the staging
-            if (mode != 2) pv(pb, stage);
-            kreads(next);
-        };
-        // the copies are unconditional (past the last tile a free stage gets
-        // the last tile again), so every barrier's vmcnt(9) is exact
-        for (int T = 0; T < n_tiles; ++T) tile(T, T & 3);
+        }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no copy outlives the pass
+    };
+    // exact row maxima (in score*c units, combined over the key halves
+    // later), no P·V; one barrier per tile as above
+    auto max_pass = [&]() __attribute__((always_inline)) {
+        float M = -INFINITY;
+        prologue();
+        for (int T = 0; T < n_tiles; ++T) {
+            float sv[4];
+            scores(T, sv);
+            M = fmaxf(M, block_row_max(sv) * a.c);
+            dma_barrier();
+            dma_tile(min(T + 3, n_tiles - 1), (T + 3) & 3);
+            if (T + 1 < n_tiles) kreads((T + 1) & 3);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         return M;
     };
 
@@ -390,18 +420,18 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
     };
 
     constexpr float kMaxL = 4294967296.0f;  // 2^32: every p <= 2^32 when l <= 2^32
-    pass(0);
+    pass(true);
     float l_row, m_row;
     finish_stats(l_row, m_row);
     // every wave holds the same 32 rows' normalizers
     const bool bad = __builtin_amdgcn_ballot_w64(!(l_row <= kMaxL)) != 0;
     if (bad) {
         // exact row maxima, then the pass again (rare)
-        float M = pass(2);
+        float M = max_pass();
         __syncthreads();
         M = combine_halves(M, true);
         m = (M == -INFINITY) ? 0.f : M;
-        pass(1);
+        pass(false);
         finish_stats(l_row, m_row);
     }
 
