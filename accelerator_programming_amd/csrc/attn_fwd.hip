@@ -116,16 +116,14 @@ hipError_t launch(const attn_fwd_plan *pl, const KernelArgs &a, hipStream_t stre
 }
 
 // Wide heads: V given as the first d_v columns of K's rows takes the kernel
-// that stages only K; any other V takes the general one. Both use 32-row
-// tiles and 256 threads.
+// that stages only K (512 threads); any other V takes the general one (the
+// plan's block). Both use 32-row tiles, so the grid is the same.
 template <bool CAUSAL>
 hipError_t launch_wide(const attn_fwd_plan *pl, const KernelArgs &a, hipStream_t stream) {
-    static_assert(attn::WideVkCfg<576, 512>::TQ == WideCfg<576, 512>::TQ &&
-                      attn::WideVkCfg<576, 512>::NT == WideCfg<576, 512>::NT,
-                  "one grid for both wide kernels");
+    static_assert(attn::WideVkCfg<576, 512>::TQ == WideCfg<576, 512>::TQ, "one grid for both wide kernels");
     if (a.v_in_k)
         hipLaunchKernelGGL((attn::attn_fwd_wide_vk_kernel<576, 512, CAUSAL>), dim3((uint32_t)pl->grid),
-                           dim3(pl->block), 0, stream, a);
+                           dim3(attn::WideVkCfg<576, 512>::NT), 0, stream, a);
     else
         hipLaunchKernelGGL((attn::attn_fwd_wide_kernel<576, 512, CAUSAL>), dim3((uint32_t)pl->grid),
                            dim3(pl->block), 0, stream, a);

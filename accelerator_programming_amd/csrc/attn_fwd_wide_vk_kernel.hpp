@@ -5,38 +5,37 @@
 // Same method as the other kernels (disjoint output tiles, "Distilling a 4.5
 // hour CUDA talk", section 5; K/V streamed through LDS with the row softmax
 // carried by a per-row reference and normalizer, section 7). What differs is
-// how the 4 waves of a workgroup share the work of one 32-row query tile and
-// a 32-key tile:
-//  * Scores: wave w = 2 rh + kh owns the 16 x 16 block of keys
-//    16 kh .. 16 kh + 15 and rows 16 rh .. 16 rh + 15 and computes it whole
-//    (Sᵀ = K·Qᵀ, 18 k-steps of v_mfma_f32_16x16x32_bf16; it holds its 16
-//    rows of Q in registers). It applies the mask and the exponential to its
-//    block only and writes P (bf16) to LDS.
+// how the 8 waves of a workgroup (two per SIMD) share the work of one 32-row
+// query tile and a 32-key tile:
+//  * Scores: waves 0..3, w = 2 rh + kh, each own the 16 x 16 block of keys
+//    16 kh .. 16 kh + 15 and rows 16 rh .. 16 rh + 15 and compute it whole
+//    (Sᵀ = K·Qᵀ, 18 k-steps of v_mfma_f32_16x16x32_bf16, their 16 rows of Q
+//    held in registers), apply the mask and the exponential to it and write
+//    P (bf16) to LDS.
+//  * Copies: waves 4..7 move the K tiles into LDS (LDS-DMA).
 //  * Values: after one barrier every wave reads all of P and accumulates
-//    output columns 128 w .. 128 w + 127 for all 32 rows (O = P·V split over
+//    output columns 64 w .. 64 w + 63 for all 32 rows (O = P·V split over
 //    the value columns), reading its Vᵀ fragments from the K tile.
-//  So no MFMA or exponential is repeated across waves (per tile a wave does
-//  18 16x16 and 8 32x32 MFMAs and 4 exponentials per lane), and the only
-//  per-tile exchange is the 2 KB of P.
+//  Each SIMD holds one score wave and one copy wave, so its MFMA work per
+//  tile is 18 16x16 + 8 32x32 MFMAs either way; no MFMA or exponential is
+//  repeated; the only per-tile exchange is the 2 KB of P. Two waves per SIMD
+//  keep more LDS requests in flight than one, and one wave's MFMAs run while
+//  the other waits.
 //  * Row statistics: the reference m of a row (the maximum over the first 32
 //    keys) and, at the end, its normalizer l are the two key halves' values
 //    combined through LDS.
-//  * K tiles (32 keys x 1152 bytes) sit in a four-stage LDS ring, filled by
-//    LDS-DMA (buffer_load ... lds): after tile T's barrier each wave copies
-//    its quarter of tile T + 3, and tile T + 2's barrier waits for it, which
-//    leaves two tiles of time for the copies. One barrier per tile: P of
-//    tile T is written to a double-buffered area before it and read after it.
+//  * K tiles (32 keys x 1152 bytes) sit in a four-stage LDS ring: after tile
+//    T's barrier each copy wave issues its quarter of tile T + 2, and the
+//    next barrier waits for it.
+//  * Software pipeline, one barrier per tile: after the barrier that
+//    publishes P of tile T, a wave issues the LDS reads of P·V(T) and (score
+//    waves) the first K fragment reads of tile T + 1's scores, then the score
+//    MFMAs of T + 1, then the P·V MFMAs of T, then P of T + 1 and the barrier.
 //  * K rows are 72 16-byte chunks. Chunk c of row r is stored at
-//    c ^ s(r), s(r) = t ^ 4 (t & 1), t = (r / 2) % 8: the 16 rows of a
-//    fragment read (ds_read_b128) fall in 16 distinct bank groups, and so do
-//    the 4 x 4 row/column pieces of a transposed Vᵀ read (ds_read_b64_tr_b16).
-//  * Software pipeline: after the barrier of tile T a wave issues the LDS
-//    reads of P·V(T) and the 18 K fragment reads of tile T + 1's scores (into
-//    registers the compiler does not allocate, v184 .. v255), then the score
-//    MFMAs of T + 1 (one assembly block that waits for each read in turn),
-//    then the P·V MFMAs of T, then P of T + 1 and the barrier. So the read
-//    latencies overlap MFMA work instead of following a barrier. (Left to
-//    itself the compiler issues each K read right before its MFMA.)
+//    c ^ s(r), s(r) = t ^ 4 (t & 1), t = (r / 2) % 8; with the k-group
+//    order below the 16 lanes served together by a fragment read
+//    (ds_read_b128) or a transposed Vᵀ read (ds_read_b64_tr_b16) hit distinct
+//    banks.
 //  * Softmax in base 2 with the per-row reference fixed by the first 32
 //    keys, exact O = acc / l and lse, and a slow pass with exact row maxima
 //    when some row's normalizer leaves [0, 2^32] (as in the main kernel).
@@ -50,8 +49,9 @@ template <int DQK, int DV>
 struct WideVkCfg {
     static constexpr int TQ = 32;  // query rows per workgroup
     static constexpr int TK = 32;  // keys per tile
-    static constexpr int NWAVE = 4;
+    static constexpr int NWAVE = 8;
     static constexpr int NT = 64 * NWAVE;
+    static constexpr int NSW = 4;  // score waves (0..3); the others copy
     static constexpr int KCH = DQK / 8;  // 16-byte chunks per K row
     static constexpr int KROW_B = 2 * DQK;
     static constexpr int KTILE_B = TK * KROW_B;
@@ -62,12 +62,13 @@ struct WideVkCfg {
     static constexpr int POFF = NSTAGE * KTILE_B;  // P buffers after the ring
     static constexpr int SOFF = POFF + 2 * PBUF_B; // row statistics: [2 key halves][32 rows] + m[32]
     static constexpr int LDS_BYTES = SOFF + 3 * TQ * 4;
-    static constexpr int KWIN_W = KTILE_B / 1024 / NWAVE;  // 1 KB pieces per wave per tile
-    static constexpr int CBW = DV / 32 / NWAVE;            // 32-column blocks of O per wave
-    static_assert(KTILE_B % (1024 * NWAVE) == 0, "tile pieces must split over the waves");
+    static constexpr int KWIN_W = KTILE_B / 1024 / (NWAVE - NSW);  // 1 KB copies per copy wave per tile
+    static constexpr int CBW = DV / 32 / NWAVE;                    // 32-column blocks of O per wave
+    static_assert(KTILE_B % (1024 * (NWAVE - NSW)) == 0, "tile pieces must split over the copy waves");
+    static_assert(KWIN_W == 9, "the barrier waits for 9 copies");
     static_assert(NKS == 18, "the score block is written for 18 k-steps");
     static_assert(KCH % 8 == 0, "the swizzle permutes aligned groups of 8 chunks");
-    static_assert(DV % (32 * NWAVE) == 0 && DV <= DQK, "value columns");
+    static_assert(CBW == 2 && DV <= DQK, "value columns 64w .. 64w + 63");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
@@ -78,66 +79,90 @@ __device__ __forceinline__ int wide_vk_chunk(int r, int c) {
 }
 
 // ---- the score block ----------------------------------------------------------
-// K fragment ks (k-step ks, ks = 0..17) sits in v[184 + 4 ks : 187 + 4 ks].
-// wide_vk_kreads reads fragment 2 j + b from kb_b + 128 j (kb0, kb1: this
-// lane's addresses of fragments 0 and 1 in the stage); wide_vk_qk waits for
-// read ks with lgkmcnt(min(17 - ks, 15)): LDS operations finish in order and
-// a wave never has more than 15 in flight, so later LDS traffic only makes
-// that wait stricter. The block ends with enough wait states for VALU, LDS
-// or memory reads of the accumulator (the compiler does not see the MFMA
-// latency through an asm statement).
-#define WIDE_VK_S(x) #x
-#define WIDE_VK_STR(x) WIDE_VK_S(x)
-#define WIDE_VK_KREAD(KS, B, J)                                                                       \
-    "ds_read_b128 v[" WIDE_VK_STR(184 + 4 * KS) ":" WIDE_VK_STR(187 + 4 * KS) "], %[kb" #B "] offset:" \
-    WIDE_VK_STR(128 * J) "\n\t"
+// K fragments go through a ring of 6 register quads in v[176:199], which the
+// compiler does not allocate: fragment ks (k-step ks, ks = 0..17) uses slot
+// ks % 6, v[176 + 4 (ks % 6) : 179 + 4 (ks % 6)]. Fragment 2 j + b is at
+// kb_b + 128 j (kb0, kb1: this lane's addresses of fragments 0 and 1 in the
+// stage). wide_vk_kreads0 reads fragments 0..5; wide_vk_qk first waits for
+// every LDS access of the wave (lgkmcnt(0): the reads of fragments 0..5 and
+// whatever the compiler issued before them; completion order across
+// different LDS read instructions is not relied on), then issues read ks + 6
+// into slot ks % 6 right after the MFMA of step ks (which took its operand
+// at issue) and waits for read ks (ks >= 1) with lgkmcnt(min(5, 17 - ks)),
+// counting only its own ds_read_b128s, which complete in order. The block
+// ends with enough wait states for VALU, LDS or memory reads of the
+// accumulator (the compiler does not see the MFMA latency through an asm
+// statement).
 #define WIDE_VK_CLOBBERS                                                                              \
-    "v184", "v185", "v186", "v187", "v188", "v189", "v190", "v191", "v192", "v193", "v194", "v195", \
-        "v196", "v197", "v198", "v199", "v200", "v201", "v202", "v203", "v204", "v205", "v206",     \
-        "v207", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215", "v216", "v217",     \
-        "v218", "v219", "v220", "v221", "v222", "v223", "v224", "v225", "v226", "v227", "v228",     \
-        "v229", "v230", "v231", "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239",     \
-        "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250",     \
-        "v251", "v252", "v253", "v254", "v255"
+    "v176", "v177", "v178", "v179", "v180", "v181", "v182", "v183", "v184", "v185", "v186", "v187", \
+        "v188", "v189", "v190", "v191", "v192", "v193", "v194", "v195", "v196", "v197", "v198", "v199"
+// read of fragment ks: slot ks % 6, base kb(ks % 2), offset 128 (ks / 2)
+#define WIDE_VK_KR0 "ds_read_b128 v[176:179], %[kb0] offset:0\n\t"
+#define WIDE_VK_KR1 "ds_read_b128 v[180:183], %[kb1] offset:0\n\t"
+#define WIDE_VK_KR2 "ds_read_b128 v[184:187], %[kb0] offset:128\n\t"
+#define WIDE_VK_KR3 "ds_read_b128 v[188:191], %[kb1] offset:128\n\t"
+#define WIDE_VK_KR4 "ds_read_b128 v[192:195], %[kb0] offset:256\n\t"
+#define WIDE_VK_KR5 "ds_read_b128 v[196:199], %[kb1] offset:256\n\t"
+#define WIDE_VK_KR6 "ds_read_b128 v[176:179], %[kb0] offset:384\n\t"
+#define WIDE_VK_KR7 "ds_read_b128 v[180:183], %[kb1] offset:384\n\t"
+#define WIDE_VK_KR8 "ds_read_b128 v[184:187], %[kb0] offset:512\n\t"
+#define WIDE_VK_KR9 "ds_read_b128 v[188:191], %[kb1] offset:512\n\t"
+#define WIDE_VK_KR10 "ds_read_b128 v[192:195], %[kb0] offset:640\n\t"
+#define WIDE_VK_KR11 "ds_read_b128 v[196:199], %[kb1] offset:640\n\t"
+#define WIDE_VK_KR12 "ds_read_b128 v[176:179], %[kb0] offset:768\n\t"
+#define WIDE_VK_KR13 "ds_read_b128 v[180:183], %[kb1] offset:768\n\t"
+#define WIDE_VK_KR14 "ds_read_b128 v[184:187], %[kb0] offset:896\n\t"
+#define WIDE_VK_KR15 "ds_read_b128 v[188:191], %[kb1] offset:896\n\t"
+#define WIDE_VK_KR16 "ds_read_b128 v[192:195], %[kb0] offset:1024\n\t"
+#define WIDE_VK_KR17 "ds_read_b128 v[196:199], %[kb1] offset:1024\n\t"
+// MFMA of step ks after waiting for its read; C: the accumulator input
+#define WIDE_VK_MM0 "s_waitcnt lgkmcnt(0)\n\tv_mfma_f32_16x16x32_bf16 %[s], v[176:179], %[q0], " "0" "\n\t"
+#define WIDE_VK_MM1 "s_waitcnt lgkmcnt(5)\n\tv_mfma_f32_16x16x32_bf16 %[s], v[180:183], %[q1], " "%[s]" "\n\t"
+#define WIDE_VK_MM2 "s_waitcnt lgkmcnt(5)\n\tv_mfma_f32_16x16x32_bf16 %[s], v[184:187], %[q2], " "%[s]" "\n\t"
+#define WIDE_VK_MM3 "s_waitcnt lgkmcnt(5)\n\tv_mfma_f32_16x16x32_bf16 %[s], v[188:191], %[q3], " "%[s]" "\n\t"
+#define WIDE_VK_MM4 "s_waitcnt lgkmcnt(5)\n\tv_mfma_f32_16x16x32_bf16 %[s], v[192:195], %[q4], " "%[s]" "\n\t"
+#define WIDE_VK_MM5 "s_waitcnt lgkmcnt(5)\n\tv_mfma_f32_16x16x32_bf16 %[s], v[196:199], %[q5], " "%[s]" "\n\t"
+#define WIDE_VK_MM6 "s_waitcnt lgkmcnt(5)\n\tv_mfma_f32_16x16x32_bf16 %[s], v[176:179], %[q6], " "%[s]" "\n\t"
+#define WIDE_VK_MM7 "s_waitcnt lgkmcnt(5)\n\tv_mfma_f32_16x16x32_bf16 %[s], v[180:183], %[q7], " "%[s]" "\n\t"
+#define WIDE_VK_MM8 "s_waitcnt lgkmcnt(5)\n\tv_mfma_f32_16x16x32_bf16 %[s], v[184:187], %[q8], " "%[s]" "\n\t"
+#define WIDE_VK_MM9 "s_waitcnt lgkmcnt(5)\n\tv_mfma_f32_16x16x32_bf16 %[s], v[188:191], %[q9], " "%[s]" "\n\t"
+#define WIDE_VK_MM10 "s_waitcnt lgkmcnt(5)\n\tv_mfma_f32_16x16x32_bf16 %[s], v[192:195], %[q10], " "%[s]" "\n\t"
+#define WIDE_VK_MM11 "s_waitcnt lgkmcnt(5)\n\tv_mfma_f32_16x16x32_bf16 %[s], v[196:199], %[q11], " "%[s]" "\n\t"
+#define WIDE_VK_MM12 "s_waitcnt lgkmcnt(5)\n\tv_mfma_f32_16x16x32_bf16 %[s], v[176:179], %[q12], " "%[s]" "\n\t"
+#define WIDE_VK_MM13 "s_waitcnt lgkmcnt(4)\n\tv_mfma_f32_16x16x32_bf16 %[s], v[180:183], %[q13], " "%[s]" "\n\t"
+#define WIDE_VK_MM14 "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_16x16x32_bf16 %[s], v[184:187], %[q14], " "%[s]" "\n\t"
+#define WIDE_VK_MM15 "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_16x16x32_bf16 %[s], v[188:191], %[q15], " "%[s]" "\n\t"
+#define WIDE_VK_MM16 "s_waitcnt lgkmcnt(1)\n\tv_mfma_f32_16x16x32_bf16 %[s], v[192:195], %[q16], " "%[s]" "\n\t"
+#define WIDE_VK_MM17 "s_waitcnt lgkmcnt(0)\n\tv_mfma_f32_16x16x32_bf16 %[s], v[196:199], %[q17], " "%[s]" "\n\t"
 
-__device__ __forceinline__ void wide_vk_kreads(uint32_t kb0, uint32_t kb1) {
-    asm volatile(WIDE_VK_KREAD(0, 0, 0) WIDE_VK_KREAD(1, 1, 0) WIDE_VK_KREAD(2, 0, 1)
-                 WIDE_VK_KREAD(3, 1, 1) WIDE_VK_KREAD(4, 0, 2) WIDE_VK_KREAD(5, 1, 2)
-                 WIDE_VK_KREAD(6, 0, 3) WIDE_VK_KREAD(7, 1, 3) WIDE_VK_KREAD(8, 0, 4)
-                 WIDE_VK_KREAD(9, 1, 4) WIDE_VK_KREAD(10, 0, 5) WIDE_VK_KREAD(11, 1, 5)
-                 WIDE_VK_KREAD(12, 0, 6) WIDE_VK_KREAD(13, 1, 6) WIDE_VK_KREAD(14, 0, 7)
-                 WIDE_VK_KREAD(15, 1, 7) WIDE_VK_KREAD(16, 0, 8) WIDE_VK_KREAD(17, 1, 8)
+__device__ __forceinline__ void wide_vk_kreads0(uint32_t kb0, uint32_t kb1) {
+    asm volatile(WIDE_VK_KR0 WIDE_VK_KR1 WIDE_VK_KR2 WIDE_VK_KR3 WIDE_VK_KR4 WIDE_VK_KR5
                  :
                  : [kb0] "v"(kb0), [kb1] "v"(kb1)
                  : WIDE_VK_CLOBBERS, "memory");
 }
 
-#define WIDE_VK_STEP(WAIT, KS, C)                                                                   \
-    "s_waitcnt lgkmcnt(" WIDE_VK_STR(WAIT) ")\n\t"                                                  \
-    "v_mfma_f32_16x16x32_bf16 %[s], v[" WIDE_VK_STR(184 + 4 * KS) ":" WIDE_VK_STR(187 + 4 * KS) "], " \
-    "%[q" #KS "], " C "\n\t"
-
-__device__ __forceinline__ f32x4 wide_vk_qk(const bf16x8 (&q)[18]) {
+__device__ __forceinline__ f32x4 wide_vk_qk(const bf16x8 (&q)[18], uint32_t kb0, uint32_t kb1) {
     f32x4 s;
-    asm volatile(WIDE_VK_STEP(15, 0, "0") WIDE_VK_STEP(15, 1, "%[s]") WIDE_VK_STEP(15, 2, "%[s]")
-                 WIDE_VK_STEP(14, 3, "%[s]") WIDE_VK_STEP(13, 4, "%[s]") WIDE_VK_STEP(12, 5, "%[s]")
-                 WIDE_VK_STEP(11, 6, "%[s]") WIDE_VK_STEP(10, 7, "%[s]") WIDE_VK_STEP(9, 8, "%[s]")
-                 WIDE_VK_STEP(8, 9, "%[s]") WIDE_VK_STEP(7, 10, "%[s]") WIDE_VK_STEP(6, 11, "%[s]")
-                 WIDE_VK_STEP(5, 12, "%[s]") WIDE_VK_STEP(4, 13, "%[s]") WIDE_VK_STEP(3, 14, "%[s]")
-                 WIDE_VK_STEP(2, 15, "%[s]") WIDE_VK_STEP(1, 16, "%[s]") WIDE_VK_STEP(0, 17, "%[s]")
+    asm volatile(WIDE_VK_MM0 WIDE_VK_KR6 WIDE_VK_MM1 WIDE_VK_KR7 WIDE_VK_MM2 WIDE_VK_KR8
+                 WIDE_VK_MM3 WIDE_VK_KR9 WIDE_VK_MM4 WIDE_VK_KR10 WIDE_VK_MM5 WIDE_VK_KR11
+                 WIDE_VK_MM6 WIDE_VK_KR12 WIDE_VK_MM7 WIDE_VK_KR13 WIDE_VK_MM8 WIDE_VK_KR14
+                 WIDE_VK_MM9 WIDE_VK_KR15 WIDE_VK_MM10 WIDE_VK_KR16 WIDE_VK_MM11 WIDE_VK_KR17
+                 WIDE_VK_MM12 WIDE_VK_MM13 WIDE_VK_MM14 WIDE_VK_MM15 WIDE_VK_MM16 WIDE_VK_MM17
                  "s_nop 7\n\ts_nop 7\n\ts_nop 3"
                  : [s] "=&a"(s)
-                 : [q0] "v"(q[0]), [q1] "v"(q[1]), [q2] "v"(q[2]), [q3] "v"(q[3]), [q4] "v"(q[4]),
+                 : [kb0] "v"(kb0), [kb1] "v"(kb1),
+                   [q0] "v"(q[0]), [q1] "v"(q[1]), [q2] "v"(q[2]), [q3] "v"(q[3]), [q4] "v"(q[4]),
                    [q5] "v"(q[5]), [q6] "v"(q[6]), [q7] "v"(q[7]), [q8] "v"(q[8]), [q9] "v"(q[9]),
                    [q10] "v"(q[10]), [q11] "v"(q[11]), [q12] "v"(q[12]), [q13] "v"(q[13]),
                    [q14] "v"(q[14]), [q15] "v"(q[15]), [q16] "v"(q[16]), [q17] "v"(q[17])
-                 : "memory");
+                 : WIDE_VK_CLOBBERS, "memory");
     return s;
 }
 
 template <int DQK, int DV, bool CAUSAL>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-__attribute__((amdgpu_num_vgpr(184)))  // v184 .. v255: the K fragments of the asm blocks
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__attribute__((amdgpu_num_vgpr(176)))  // v176 .. v199: the K fragment ring of the asm blocks
 attn_fwd_wide_vk_kernel(const KernelArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
     using C = WideVkCfg<DQK, DV>;
@@ -147,14 +172,15 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool sw = w < C::NSW;                  // a score wave (else a copy wave)
     const int l32 = lane & 31, g = lane >> 5;    // 32x32 fragments (P·V)
     const int l16 = lane & 15, G = lane >> 4;    // 16x16 fragments (scores)
-    const int kh = w & 1, rh = w >> 1;           // this wave's score block
+    const int kh = w & 1, rh = (w >> 1) & 1;     // a score wave's block
     // k-group of this lane's 8 contraction elements in a k-step: quarter G
     // takes group (G % 2) * 2 + G / 2, so that the two quarters whose LDS
     // reads are served together (lanes i and i + 32) read chunks 4 ks + x and
-    // 4 ks + x + 1 (x even): with the row swizzle below the 16 lanes of such a
-    // pass then hit distinct banks. Q uses the same assignment.
+    // 4 ks + x + 1 (x even): with the row swizzle the 16 lanes of such a pass
+    // then hit distinct banks. Q uses the same assignment.
     const int kg = ((G & 1) << 1) | (G >> 1);
 
     // ---- work item ----------------------------------------------------------
@@ -175,46 +201,51 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
     // tiles from this index on need the causal or key-range mask
     const int first_masked = CAUSAL ? min(q0 / TK, a.Nkv / TK) : a.Nkv / TK;
 
-    // ---- Q of the block's 16 rows (B operands), resident throughout ---------
+    // ---- Q of the block's 16 rows (B operands, score waves), resident -------
     bf16x8 qf[C::NKS];
 #pragma unroll
     for (int ks = 0; ks < C::NKS; ++ks) {
         u32x4 v = {0, 0, 0, 0};
-        if (srow < a.Nq) v = load8_bf16(Qp + (int64_t)srow * a.q_sn + 32 * ks + 8 * kg);
+        if (sw && srow < a.Nq) v = load8_bf16(Qp + (int64_t)srow * a.q_sn + 32 * ks + 8 * kg);
         qf[ks] = u32x4_as_bf16x8(v);
     }
 
-    // ---- K staging: piece u of wave w is the 1 KB at (4u + w) KB of the tile;
-    // lane i moves its 16-byte unit 64 (4u + w) + i, which holds the logical
-    // chunk the swizzle puts there. The byte offsets inside a tile are the
-    // same for every tile; the copies go through a buffer resource that ends
-    // at the last key, so rows past it read as zeros (finite, masked). -----
+    // ---- K copies (copy waves): piece u of copy wave c = w - 4 is the 1 KB at
+    // (4u + c) KB of the tile; lane i moves its 16-byte unit 64 (4u + c) + i,
+    // which holds the logical chunk the swizzle puts there. The byte offsets
+    // inside a tile are the same for every tile; the copies go through a
+    // buffer resource that ends at the last key, so rows past it read as
+    // zeros (finite, masked). --------------------------------------------
+    const int cw = w - C::NSW;
     uint32_t koff[C::KWIN_W];
 #pragma unroll
     for (int u = 0; u < C::KWIN_W; ++u) {
-        const int p = (C::NWAVE * u + w) * 64 + lane;
+        const int p = (4 * u + cw) * 64 + lane;
         const int r = p / C::KCH, c = wide_vk_chunk(r, p % C::KCH);
         koff[u] = (uint32_t)r * (uint32_t)a.k_sn * 2u + 16u * (uint32_t)c;
     }
-    // LDS-DMA of tile T into a stage: 9 buffer_load ... lds per wave, each
-    // 1 KB, counted by vmcnt (nothing else in the loop uses it).
+    // LDS-DMA of tile T into a stage: 9 buffer_load ... lds per copy wave,
+    // each 1 KB, counted by vmcnt (nothing else in the loop uses it)
     auto dma_tile = [&](int T, int stage) __attribute__((always_inline)) {
+        if (sw) return;
         const int rem = a.Nkv - T * TK;  // keys left, >= 1
         const u32x4 rk = buffer_rsrc(Kp + (int64_t)T * TK * a.k_sn,
                                      (uint32_t)(((int64_t)(rem - 1) * a.k_sn + DQK) * 2));
         unsigned char *st = lds + stage * C::KTILE_B;
 #pragma unroll
-        for (int u = 0; u < C::KWIN_W; ++u) dma16_buf_to_lds(rk, koff[u], st + (C::NWAVE * u + w) * 1024);
+        for (int u = 0; u < C::KWIN_W; ++u) dma16_buf_to_lds(rk, koff[u], st + (4 * u + cw) * 1024);
     };
-    // this wave's LDS accesses are done, then every wave reaches this point;
-    // DMAs stay in flight (also a compiler memory barrier)
+    // this wave's LDS accesses are done, then every wave reaches this point
+    // (also a compiler memory barrier)
     auto lds_barrier = [&]() __attribute__((always_inline)) {
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     };
-    // the same, after this wave's DMAs but the newest tile's (9) have landed:
-    // each wave waits for its own share, the barrier covers all shares
+    // the same, after all of this wave's copies have landed: each copy wave
+    // waits for its own share, the barrier covers all (a score wave has none
+    // in flight). Waiting for all (vmcnt(0)) rather than all but the newest
+    // tile's: a partial count did not order the LDS-DMA writes.
     auto dma_barrier = [&]() __attribute__((always_inline)) {
-        asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     };
 
     // ---- K fragment addresses: key row r = 16 kh + l16, chunk 4 ks + kg. With
@@ -228,9 +259,6 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
         kb[0] = base + 64 * (0 ^ (s >> 2));
         kb[1] = base + 64 * (1 ^ (s >> 2));
     }
-    auto kreads = [&](int stage) __attribute__((always_inline)) {
-        wide_vk_kreads(kb[0] + stage * C::KTILE_B, kb[1] + stage * C::KTILE_B);
-    };
 
     // ---- P layout: row-major, 80-byte rows (conflict-free 16-byte reads of 16
     // rows); within each 16-key chunk key 4 q + i (q < 4, i < 4) sits at
@@ -243,35 +271,33 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
     // ---- state -------------------------------------------------------------
     f32x16 oacc[CBW];
     float m = 0.f;  // reference of row srow (score*c units), same in both key halves
-    float l;        // normalizer of row srow over this lane's keys
+    float l;        // normalizer of row srow over this lane's keys (score waves)
     float *stat = (float *)(lds + C::SOFF);  // [kh][32] per-half row values, then m[32]
 
-    // ---- Vᵀ fragments (value columns 32 db .. 32 db + 31, keys 16 kc ..
-    // 16 kc + 15, db = 4w + i): two transposed reads (key halves hr) of the K
-    // tile, whose rows begin with the values. Lane (4 g + i16 / 4 + 8 hr + 16 kc,
-    // column 32 db + 16 (G % 2) + 4 (i16 % 4)) reads 4 values. The row's
-    // swizzle s does not depend on kc, and XOR-ing the chunk 4 db + x (x < 4)
-    // with s gives 4 (db ^ s/4) + (x ^ s%4): the address of (i, kc, hr) is
-    // vtb[hr][i % 2] + 128 (i / 2) + 16 rows (kc). -------------------------
-    static_assert(CBW == 4, "column blocks 4w + i, i < 4");
-    uint32_t vtb[2][2];
+    // ---- Vᵀ fragments (value columns 32 db .. 32 db + 31, db = 2w + i, keys
+    // 16 kc .. 16 kc + 15): two transposed reads (key halves hr) of the K tile,
+    // whose rows begin with the values. Lane (4 g + i16 / 4 + 8 hr + 16 kc,
+    // column 32 db + 16 (G % 2) + 4 (i16 % 4)) reads 4 values; the row's
+    // swizzle does not depend on kc, so (i, kc, hr) is at vtb[hr][i] + 16
+    // rows (kc). ------------------------------------------------------------
+    uint32_t vtb[2][CBW];
     {
         const int i16 = lane & 15;
 #pragma unroll
         for (int hr = 0; hr < 2; ++hr)
 #pragma unroll
-            for (int ip = 0; ip < 2; ++ip) {
+            for (int i = 0; i < CBW; ++i) {
                 const int vr = 8 * hr + 4 * g + (i16 >> 2);
-                const int col = 32 * (CBW * w + ip) + 16 * (G & 1) + 4 * (i16 & 3);
-                vtb[hr][ip] = (uint32_t)(uintptr_t)(lds_void *)lds +
-                              (uint32_t)(vr * C::KROW_B + 16 * wide_vk_chunk(vr, col >> 3) + 2 * (col & 7));
+                const int col = 32 * (CBW * w + i) + 16 * (G & 1) + 4 * (i16 & 3);
+                vtb[hr][i] = (uint32_t)(uintptr_t)(lds_void *)lds +
+                             (uint32_t)(vr * C::KROW_B + 16 * wide_vk_chunk(vr, col >> 3) + 2 * (col & 7));
             }
     }
     auto vt_frag_k = [&](uint32_t stage_off, int i, int kc) __attribute__((always_inline)) {
         i16x4 hv[2];
 #pragma unroll
         for (int hr = 0; hr < 2; ++hr) {
-            const uint32_t addr = vtb[hr][i & 1] + stage_off + 128 * (i >> 1) + 16 * C::KROW_B * kc;
+            const uint32_t addr = vtb[hr][i] + stage_off + 16 * C::KROW_B * kc;
             hv[hr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(uintptr_t)addr);
         }
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(hv[0], hv[1], 0, 1, 2, 3, 4, 5, 6, 7));
@@ -301,17 +327,18 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
         x = fmaxf(x, __shfl_xor(x, 32));
         return x;
     };
-    // combine a per-row value of the two key halves: both halves' waves get
-    // v(half 0) op v(half 1) (one barrier); returns it for row srow
+    // combine a per-row value of the two key halves (score waves give it; one
+    // barrier for all waves); returns v(half 0) op v(half 1) for row srow
     auto combine_halves = [&](float v, bool is_max) __attribute__((always_inline)) {
-        if (G == 0) stat[32 * kh + 16 * rh + l16] = v;
+        if (sw && G == 0) stat[32 * kh + 16 * rh + l16] = v;
         lds_barrier();
         const float v0 = stat[16 * rh + l16], v1 = stat[32 + 16 * rh + l16];
         return is_max ? fmaxf(v0, v1) : v0 + v1;
     };
-    // the score block of tile T (its K fragments already read), masked
-    auto scores = [&](int T, float (&sv)[4]) __attribute__((always_inline)) {
-        const f32x4 sacc = wide_vk_qk(qf);
+    // the score block of tile T (its first K fragment reads issued), masked
+    auto scores = [&](int T, int stage, float (&sv)[4]) __attribute__((always_inline)) {
+        const uint32_t so = stage * C::KTILE_B;
+        const f32x4 sacc = wide_vk_qk(qf, kb[0] + so, kb[1] + so);
 #pragma unroll
         for (int i = 0; i < 4; ++i) sv[i] = sacc[i];
         if (T >= first_masked) {
@@ -322,6 +349,10 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
             }
         }
     };
+    auto kreads0 = [&](int stage) __attribute__((always_inline)) {
+        const uint32_t so = stage * C::KTILE_B;
+        wide_vk_kreads0(kb[0] + so, kb[1] + so);
+    };
     // P of the block (bf16) into tile T's P buffer, and l
     auto block_p = [&](int T, const float (&sv)[4]) __attribute__((always_inline)) {
         const float negm = -m;
@@ -331,26 +362,23 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
         l = sum_bf16x2(p23, sum_bf16x2(p01, l));
         *(u32x2 *)(lds + C::POFF + (T & 1) * C::PBUF_B + p_wr) = u32x2{p01, p23};
     };
-    // tiles 0, 1, 2 into stages 0, 1, 2; tile 0 landed everywhere; its K
-    // fragment reads issued
+    // tiles 0, 1 into stages 0, 1, landed everywhere; the score waves' first
+    // K fragment reads issued
     auto prologue = [&]() __attribute__((always_inline)) {
         __syncthreads();  // the ring, the P buffers and the statistics are free
         dma_tile(0, 0);
         dma_tile(min(1, n_tiles - 1), 1);
-        dma_tile(min(2, n_tiles - 1), 2);
-        asm volatile("s_waitcnt vmcnt(18)\n\ts_barrier" ::: "memory");
-        kreads(0);
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        if (sw) kreads0(0);
     };
 
     // ---- one pass over the keys: O and l (set_m: the reference from tile 0)
     // Tile T's stage is T % 4. Software pipeline, one barrier per tile:
-    //   [P·V reads of T] [K reads of T + 1] [copy of T + 3] [scores of T + 1]
+    //   [P·V reads of T] [K reads of T + 1 | copy of T + 2] [scores of T + 1]
     //   [P·V MFMAs of T] [P of T + 1] barrier
-    // The barrier that publishes P of T + 1 also waits for this wave's copy
-    // of tile T + 2 (two tiles old); the copy of T + 3 goes into the stage of
-    // tile T - 1, which every wave finished before the previous barrier. The
-    // copies are unconditional (past the last tile a free stage gets the last
-    // tile again), so every vmcnt(9) is exact.
+    // The barrier that publishes P of T + 1 also waits for the copy of tile
+    // T + 2 (issued one tile earlier), which goes into the stage of tile
+    // T - 2, finished by every wave two barriers before.
     auto pass = [&](bool set_m) __attribute__((always_inline)) {
         l = 0.f;
 #pragma unroll
@@ -359,45 +387,47 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
             for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
         prologue();
         {
-            float sv[4];
-            scores(0, sv);
+            float sv[4] = {0.f, 0.f, 0.f, 0.f};
+            if (sw) scores(0, 0, sv);
             if (set_m) {
                 // reference: the row maximum over tile 0 (an extra barrier,
                 // the same in every wave)
-                const float mx = combine_halves(block_row_max(sv), true) * a.c;
+                const float mx = combine_halves(sw ? block_row_max(sv) : 0.f, true) * a.c;
                 m = (mx == -INFINITY) ? 0.f : mx;
             }
-            block_p(0, sv);
+            if (sw) block_p(0, sv);
             dma_barrier();
         }
         for (int T = 0; T < n_tiles; ++T) {
             const bool more = T + 1 < n_tiles;
             bf16x8 pf[2], vf[2][CBW];
             pv_reads(lds + C::POFF + (T & 1) * C::PBUF_B, T & 3, pf, vf);
-            if (more) kreads((T + 1) & 3);
-            dma_tile(min(T + 3, n_tiles - 1), (T + 3) & 3);
-            float sv[4];
-            if (more) scores(T + 1, sv);
+            if (sw && more) kreads0((T + 1) & 3);
+            if (T + 2 < n_tiles) dma_tile(T + 2, (T + 2) & 3);
+            float sv[4] = {0.f, 0.f, 0.f, 0.f};
+            if (sw && more) scores(T + 1, (T + 1) & 3, sv);
             pv_mma(pf, vf);
             if (more) {
-                block_p(T + 1, sv);
+                if (sw) block_p(T + 1, sv);
                 dma_barrier();
             }
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no copy outlives the pass
     };
-    // exact row maxima (in score*c units, combined over the key halves
-    // later), no P·V; one barrier per tile as above
+    // exact row maxima (in score*c units; score waves), no P·V; one barrier
+    // per tile as above
     auto max_pass = [&]() __attribute__((always_inline)) {
         float M = -INFINITY;
         prologue();
         for (int T = 0; T < n_tiles; ++T) {
-            float sv[4];
-            scores(T, sv);
-            M = fmaxf(M, block_row_max(sv) * a.c);
+            if (sw) {
+                float sv[4];
+                scores(T, T & 3, sv);
+                M = fmaxf(M, block_row_max(sv) * a.c);
+            }
+            if (T + 2 < n_tiles) dma_tile(T + 2, (T + 2) & 3);
             dma_barrier();
-            dma_tile(min(T + 3, n_tiles - 1), (T + 3) & 3);
-            if (T + 1 < n_tiles) kreads((T + 1) & 3);
+            if (sw && T + 1 < n_tiles) kreads0((T + 1) & 3);
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         return M;
@@ -410,7 +440,7 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
         x += __shfl_xor(x, 16);
         x += __shfl_xor(x, 32);
         __syncthreads();  // the statistics area is free
-        if (G == 0) {
+        if (sw && G == 0) {
             stat[32 * kh + 16 * rh + l16] = x;
             if (kh == 0) stat[64 + 16 * rh + l16] = m;
         }

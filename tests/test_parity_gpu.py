@@ -103,6 +103,11 @@ WIDE = [
     (1, 2, 2, 45, 45, True, False),
     (2, 3, 1, 100, 100, True, True),
     (1, 2, 1, 33, 257, False, False),
+    # V inside K over several tiles: the K ring's stages and P buffers are
+    # reused and the copies of later tiles land while earlier ones are read
+    (1, 2, 1, 32, 96, False, True),
+    (1, 2, 1, 64, 200, False, True),
+    (1, 3, 1, 64, 333, True, True),
 ]
 
 
