@@ -25,8 +25,8 @@
 //    keys) and, at the end, its normalizer l are the two key halves' values
 //    combined through LDS.
 //  * K tiles (32 keys x 1152 bytes) sit in a four-stage LDS ring: after tile
-//    T's barrier each copy wave issues its quarter of tile T + 2, and the
-//    next barrier waits for it.
+//    T's barrier one pair of copy waves issues tile T + 3 (the pairs take
+//    turns), and the barrier two tiles later waits for it.
 //  * Software pipeline, one barrier per tile: after the barrier that
 //    publishes P of tile T, a wave issues the LDS reads of P·V(T) and (score
 //    waves) the first K fragment reads of tile T + 1's scores, then the score
@@ -62,10 +62,10 @@ struct WideVkCfg {
     static constexpr int POFF = NSTAGE * KTILE_B;  // P buffers after the ring
     static constexpr int SOFF = POFF + 2 * PBUF_B; // row statistics: [2 key halves][32 rows] + m[32]
     static constexpr int LDS_BYTES = SOFF + 3 * TQ * 4;
-    static constexpr int KWIN_W = KTILE_B / 1024 / (NWAVE - NSW);  // 1 KB copies per copy wave per tile
+    static constexpr int KWIN_W = KTILE_B / 1024 / 2;  // 1 KB copies per copy wave per copied tile
     static constexpr int CBW = DV / 32 / NWAVE;                    // 32-column blocks of O per wave
-    static_assert(KTILE_B % (1024 * (NWAVE - NSW)) == 0, "tile pieces must split over the copy waves");
-    static_assert(KWIN_W == 9, "the barrier waits for 9 copies");
+    static_assert(NWAVE - NSW == 4, "two pairs of copy waves");
+    static_assert(KTILE_B % 2048 == 0, "tile pieces must split over a pair of copy waves");
     static_assert(NKS == 18, "the score block is written for 18 k-steps");
     static_assert(KCH % 8 == 0, "the swizzle permutes aligned groups of 8 chunks");
     static_assert(CBW == 2 && DV <= DQK, "value columns 64w .. 64w + 63");
@@ -210,42 +210,47 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
         qf[ks] = u32x4_as_bf16x8(v);
     }
 
-    // ---- K copies (copy waves): piece u of copy wave c = w - 4 is the 1 KB at
-    // (4u + c) KB of the tile; lane i moves its 16-byte unit 64 (4u + c) + i,
-    // which holds the logical chunk the swizzle puts there. The byte offsets
-    // inside a tile are the same for every tile; the copies go through a
-    // buffer resource that ends at the last key, so rows past it read as
-    // zeros (finite, masked). --------------------------------------------
-    const int cw = w - C::NSW;
+    // ---- K copies: copy waves 4, 5 copy the even tiles, 6, 7 the odd ones,
+    // so that a pair's copies of a tile are its only ones in flight when it
+    // waits for them (vmcnt(0)) two tiles later. Piece u of pair member m is
+    // the 1 KB at (2u + m) KB of the tile; lane i moves its 16-byte unit
+    // 64 (2u + m) + i, which holds the logical chunk the swizzle puts there.
+    // The byte offsets inside a tile are the same for every tile; the copies
+    // go through a buffer resource that ends at the last key, so rows past it
+    // read as zeros (finite, masked). -------------------------------------
+    const int cpair = ((w - C::NSW) >> 1) & 1, cm = (w - C::NSW) & 1;
     uint32_t koff[C::KWIN_W];
 #pragma unroll
     for (int u = 0; u < C::KWIN_W; ++u) {
-        const int p = (4 * u + cw) * 64 + lane;
+        const int p = (2 * u + cm) * 64 + lane;
         const int r = p / C::KCH, c = wide_vk_chunk(r, p % C::KCH);
         koff[u] = (uint32_t)r * (uint32_t)a.k_sn * 2u + 16u * (uint32_t)c;
     }
-    // LDS-DMA of tile T into a stage: 9 buffer_load ... lds per copy wave,
-    // each 1 KB, counted by vmcnt (nothing else in the loop uses it)
+    // LDS-DMA of tile T into a stage by the pair T % 2: 18 buffer_load ...
+    // lds per wave, each 1 KB, counted by vmcnt (nothing else in the loop
+    // uses it)
     auto dma_tile = [&](int T, int stage) __attribute__((always_inline)) {
-        if (sw) return;
+        if (sw || (T & 1) != cpair) return;
         const int rem = a.Nkv - T * TK;  // keys left, >= 1
         const u32x4 rk = buffer_rsrc(Kp + (int64_t)T * TK * a.k_sn,
                                      (uint32_t)(((int64_t)(rem - 1) * a.k_sn + DQK) * 2));
         unsigned char *st = lds + stage * C::KTILE_B;
 #pragma unroll
-        for (int u = 0; u < C::KWIN_W; ++u) dma16_buf_to_lds(rk, koff[u], st + (4 * u + cw) * 1024);
+        for (int u = 0; u < C::KWIN_W; ++u) dma16_buf_to_lds(rk, koff[u], st + (2 * u + cm) * 1024);
     };
     // this wave's LDS accesses are done, then every wave reaches this point
     // (also a compiler memory barrier)
     auto lds_barrier = [&]() __attribute__((always_inline)) {
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     };
-    // the same, after all of this wave's copies have landed: each copy wave
-    // waits for its own share, the barrier covers all (a score wave has none
-    // in flight). Waiting for all (vmcnt(0)) rather than all but the newest
-    // tile's: a partial count did not order the LDS-DMA writes.
-    auto dma_barrier = [&]() __attribute__((always_inline)) {
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // the same, where the pair that copies tile Tw first waits for all its
+    // copies (vmcnt(0): a partial count did not order the LDS-DMA writes);
+    // the barrier then publishes tile Tw to every wave
+    auto copy_barrier = [&](int Tw) __attribute__((always_inline)) {
+        if (!sw && (Tw & 1) == cpair)
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        else
+            lds_barrier();
     };
 
     // ---- K fragment addresses: key row r = 16 kh + l16, chunk 4 ks + kg. With
@@ -362,23 +367,22 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
         l = sum_bf16x2(p23, sum_bf16x2(p01, l));
         *(u32x2 *)(lds + C::POFF + (T & 1) * C::PBUF_B + p_wr) = u32x2{p01, p23};
     };
-    // tiles 0, 1 into stages 0, 1, landed everywhere; the score waves' first
-    // K fragment reads issued
+    // tiles 0, 1, 2 into stages 0, 1, 2, landed everywhere; the score waves'
+    // first K fragment reads issued
     auto prologue = [&]() __attribute__((always_inline)) {
         __syncthreads();  // the ring, the P buffers and the statistics are free
-        dma_tile(0, 0);
-        dma_tile(min(1, n_tiles - 1), 1);
+        for (int T = 0; T < 3 && T < n_tiles; ++T) dma_tile(T, T);
         asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
         if (sw) kreads0(0);
     };
 
     // ---- one pass over the keys: O and l (set_m: the reference from tile 0)
     // Tile T's stage is T % 4. Software pipeline, one barrier per tile:
-    //   [P·V reads of T] [K reads of T + 1 | copy of T + 2] [scores of T + 1]
+    //   [P·V reads of T] [K reads of T + 1 | copy of T + 3] [scores of T + 1]
     //   [P·V MFMAs of T] [P of T + 1] barrier
-    // The barrier that publishes P of T + 1 also waits for the copy of tile
-    // T + 2 (issued one tile earlier), which goes into the stage of tile
-    // T - 2, finished by every wave two barriers before.
+    // The copy of T + 3 goes into the stage of tile T - 1, which every wave
+    // finished before this tile's barrier; the barrier at the end publishes
+    // tile T + 2, whose copies were issued two tiles earlier.
     auto pass = [&](bool set_m) __attribute__((always_inline)) {
         l = 0.f;
 #pragma unroll
@@ -396,20 +400,20 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
                 m = (mx == -INFINITY) ? 0.f : mx;
             }
             if (sw) block_p(0, sv);
-            dma_barrier();
+            lds_barrier();  // tile 1 landed in the prologue
         }
         for (int T = 0; T < n_tiles; ++T) {
             const bool more = T + 1 < n_tiles;
             bf16x8 pf[2], vf[2][CBW];
             pv_reads(lds + C::POFF + (T & 1) * C::PBUF_B, T & 3, pf, vf);
             if (sw && more) kreads0((T + 1) & 3);
-            if (T + 2 < n_tiles) dma_tile(T + 2, (T + 2) & 3);
+            if (T + 3 < n_tiles) dma_tile(T + 3, (T + 3) & 3);
             float sv[4] = {0.f, 0.f, 0.f, 0.f};
             if (sw && more) scores(T + 1, (T + 1) & 3, sv);
             pv_mma(pf, vf);
             if (more) {
                 if (sw) block_p(T + 1, sv);
-                dma_barrier();
+                copy_barrier(T + 2);
             }
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no copy outlives the pass
@@ -425,8 +429,8 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
                 scores(T, T & 3, sv);
                 M = fmaxf(M, block_row_max(sv) * a.c);
             }
-            if (T + 2 < n_tiles) dma_tile(T + 2, (T + 2) & 3);
-            dma_barrier();
+            if (T + 3 < n_tiles) dma_tile(T + 3, (T + 3) & 3);
+            copy_barrier(T + 1);
             if (sw && T + 1 < n_tiles) kreads0((T + 1) & 3);
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");

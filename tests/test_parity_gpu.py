@@ -107,7 +107,7 @@ WIDE = [
     # reused and the copies of later tiles land while earlier ones are read
     (1, 2, 1, 32, 96, False, True),
     (1, 2, 1, 64, 200, False, True),
-    (1, 3, 1, 64, 333, True, True),
+    (1, 3, 1, 333, 333, True, True),
 ]
 
 
