@@ -62,6 +62,12 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd_destroy.argtypes = [P]
         L.attn_status_str.restype = ctypes.c_char_p
         L.attn_status_str.argtypes = [ctypes.c_int]
+        L.attn_fwd_split_count.restype = ctypes.c_int32
+        L.attn_fwd_split_count.argtypes = [P]
+        L.attn_fwd_split_workspace_bytes.restype = I64
+        L.attn_fwd_split_workspace_bytes.argtypes = [P, ctypes.c_int32]
+        L.attn_fwd_run_split.restype = ctypes.c_int
+        L.attn_fwd_run_split.argtypes = [P, P, P, P, P, P, ctypes.c_int32, P, I64, P]
         L.attn_fwd_plan_info.restype = ctypes.c_int
         L.attn_fwd_plan_info.argtypes = [P, ctypes.POINTER(I64), ctypes.POINTER(ctypes.c_int32),
                                          ctypes.POINTER(ctypes.c_int32),
@@ -100,6 +106,24 @@ def attn_fwd_run(plan: int, Q: int, K: int, V: int, O: int, lse: int | None,
     st = lib().attn_fwd_run(plan, Q, K, V, O, lse or None, stream or None)
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd_run")
+
+
+def attn_fwd_split_count(plan: int) -> int:
+    """Key ranges the library would use for the plan; 0 if the split path
+    does not serve it."""
+    return int(lib().attn_fwd_split_count(plan))
+
+
+def attn_fwd_split_workspace_bytes(plan: int, n_splits: int = 0) -> int:
+    return int(lib().attn_fwd_split_workspace_bytes(plan, int(n_splits)))
+
+
+def attn_fwd_run_split(plan: int, Q: int, K: int, V: int, O: int, lse: int | None, n_splits: int,
+                       workspace: int, workspace_bytes: int, stream: int | None) -> None:
+    st = lib().attn_fwd_run_split(plan, Q, K, V, O, lse or None, int(n_splits), workspace,
+                                  int(workspace_bytes), stream or None)
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_run_split")
 
 
 def attn_fwd_destroy(plan: int | None) -> None:
@@ -180,6 +204,31 @@ class AttnFwd:
                      lse.data_ptr() if lse is not None else None, s.cuda_stream)
 
     __call__ = run
+
+    def split_count(self) -> int:
+        return attn_fwd_split_count(self.plan)
+
+    def run_split(self, q, k, v, o, lse=None, n_splits: int = 0, workspace=None,
+                  stream=None) -> None:
+        """The split-KV path; workspace (a device tensor of at least
+        attn_fwd_split_workspace_bytes bytes) is allocated with torch when
+        not given."""
+        import torch
+        for t in (q, k, v, o) + ((lse,) if lse is not None else ()):
+            if not t.is_cuda:
+                raise ValueError("attn_fwd_run_split needs device tensors")
+        if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
+            raise ValueError("lse must be a contiguous float32 tensor")
+        need = attn_fwd_split_workspace_bytes(self.plan, n_splits)
+        if need < 0:
+            raise AttnError(ATTN_ERR_UNSUPPORTED, "attn_fwd_split_workspace_bytes")
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        s = stream if stream is not None else torch.cuda.current_stream()
+        attn_fwd_run_split(self.plan, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                           lse.data_ptr() if lse is not None else None, n_splits,
+                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                           s.cuda_stream)
 
     def close(self) -> None:
         if self.plan:

@@ -12,6 +12,7 @@
 #include "attn_fwd_kernel.hpp"
 #include "attn_fwd_wide_kernel.hpp"
 #include "attn_fwd_wide_vk_kernel.hpp"
+#include "attn_split_kernel.hpp"
 
 using attn::KernelArgs;
 using attn::TileCfg;
@@ -132,6 +133,91 @@ hipError_t launch_wide(const attn_fwd_plan *pl, const KernelArgs &a, hipStream_t
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Kernel arguments of a plan and a set of device pointers.
+KernelArgs make_args(const attn_fwd_plan *plan, const void *Q, const void *K, const void *V, void *O,
+                     float *lse) {
+    const attn_fwd_params &p = plan->p;
+    KernelArgs a;
+    a.q = Q;
+    a.k = K;
+    a.v = V;
+    a.o = O;
+    a.lse = lse;
+    a.q_sb = p.q_strides[0];
+    a.q_sh = p.q_strides[1];
+    a.q_sn = (int32_t)p.q_strides[2];
+    a.k_sb = p.k_strides[0];
+    a.k_sh = p.k_strides[1];
+    a.k_sn = (int32_t)p.k_strides[2];
+    a.v_sb = p.v_strides[0];
+    a.v_sh = p.v_strides[1];
+    a.v_sn = (int32_t)p.v_strides[2];
+    a.o_sb = p.o_strides[0];
+    a.o_sh = p.o_strides[1];
+    a.o_sn = (int32_t)p.o_strides[2];
+    a.B = (int32_t)p.B;
+    a.Hq = (int32_t)p.H_q;
+    a.Hkv = (int32_t)p.H_kv;
+    a.Nq = (int32_t)p.N;
+    a.Nkv = (int32_t)p.N_kv;
+    a.group = (int32_t)(p.H_q / p.H_kv);
+    a.n_qtiles = (int32_t)plan->n_qtiles;
+    a.c = plan->c;
+    a.v_in_k = (V == K && p.v_strides[0] == p.k_strides[0] && p.v_strides[1] == p.k_strides[1] &&
+                p.v_strides[2] == p.k_strides[2]) ? 1 : 0;
+    return a;
+}
+
+// ---- split-KV path (few query rows per kv head, non-causal) ----------------
+constexpr int32_t kMaxSplits = 64;  // the merge holds one split per lane
+
+bool split_supported(const attn_fwd_plan *pl) {
+    const attn_fwd_params &p = pl->p;
+    return (pl->variant == V_D64_BF16 || pl->variant == V_D128_BF16) && !p.causal &&
+           (p.H_q / p.H_kv) * p.N <= attn::SplitCfg<64>::ROWS;
+}
+
+// about two workgroups per CU (256 CUs), at least one 64-key tile per split
+int32_t auto_splits(const attn_fwd_plan *pl) {
+    const attn_fwd_params &p = pl->p;
+    const int64_t groups = p.B * p.H_kv;
+    const int64_t tiles = (p.N_kv + 63) / 64;
+    int64_t n = (512 + groups - 1) / groups;
+    if (n > tiles) n = tiles;
+    if (n > kMaxSplits) n = kMaxSplits;
+    return (int32_t)(n < 1 ? 1 : n);
+}
+
+// workspace: n_splits partial outputs [n][B][H_q][N][d_v] fp32, then their
+// logsumexps [n][B][H_q][N] fp32
+int64_t split_workspace(const attn_fwd_plan *pl, int32_t n) {
+    const attn_fwd_params &p = pl->p;
+    return (int64_t)n * p.B * p.H_q * p.N * (p.d_v + 1) * 4;
+}
+
+template <int D>
+hipError_t launch_split(const attn_fwd_plan *pl, const KernelArgs &a, int32_t n, float *ws,
+                        hipStream_t stream) {
+    using SC = attn::SplitCfg<D>;
+    const attn_fwd_params &p = pl->p;
+    const int64_t rows = p.B * p.H_q * p.N;
+    attn::SplitArgs sa;
+    sa.a = a;
+    sa.opart = ws;
+    sa.lpart = ws + (int64_t)n * rows * D;
+    sa.n_splits = n;
+    const int64_t tiles = (p.N_kv + SC::TK - 1) / SC::TK;
+    sa.split_len = (int32_t)(((tiles + n - 1) / n) * SC::TK);
+    sa.rows = (int32_t)((p.H_q / p.H_kv) * p.N);
+    hipLaunchKernelGGL((attn::attn_split_kernel<D>), dim3((uint32_t)(n * p.B * p.H_kv)), dim3(SC::NT), 0,
+                       stream, sa);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn::attn_split_merge<D>), dim3((uint32_t)((rows + 3) / 4)), dim3(256), 0, stream,
+                       (const float *)sa.opart, (const float *)sa.lpart, n, rows, a);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 extern "C" {
@@ -170,34 +256,7 @@ attn_status attn_fwd_run(const attn_fwd_plan *plan, const void *Q, const void *K
         (lse && ((uintptr_t)lse & 3u)))
         return ATTN_ERR_INVALID;
     const attn_fwd_params &p = plan->p;
-    KernelArgs a;
-    a.q = Q;
-    a.k = K;
-    a.v = V;
-    a.o = O;
-    a.lse = lse;
-    a.q_sb = p.q_strides[0];
-    a.q_sh = p.q_strides[1];
-    a.q_sn = (int32_t)p.q_strides[2];
-    a.k_sb = p.k_strides[0];
-    a.k_sh = p.k_strides[1];
-    a.k_sn = (int32_t)p.k_strides[2];
-    a.v_sb = p.v_strides[0];
-    a.v_sh = p.v_strides[1];
-    a.v_sn = (int32_t)p.v_strides[2];
-    a.o_sb = p.o_strides[0];
-    a.o_sh = p.o_strides[1];
-    a.o_sn = (int32_t)p.o_strides[2];
-    a.B = (int32_t)p.B;
-    a.Hq = (int32_t)p.H_q;
-    a.Hkv = (int32_t)p.H_kv;
-    a.Nq = (int32_t)p.N;
-    a.Nkv = (int32_t)p.N_kv;
-    a.group = (int32_t)(p.H_q / p.H_kv);
-    a.n_qtiles = (int32_t)plan->n_qtiles;
-    a.c = plan->c;
-    a.v_in_k = (V == K && p.v_strides[0] == p.k_strides[0] && p.v_strides[1] == p.k_strides[1] &&
-                p.v_strides[2] == p.k_strides[2]) ? 1 : 0;
+    const KernelArgs a = make_args(plan, Q, K, V, O, lse);
 
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
@@ -231,6 +290,36 @@ const char *attn_status_str(attn_status status) {
         case ATTN_ERR_NOMEM: return "ATTN_ERR_NOMEM";
     }
     return "ATTN_ERR_UNKNOWN";
+}
+
+int32_t attn_fwd_split_count(const attn_fwd_plan *plan) {
+    if (!plan || !split_supported(plan)) return 0;
+    return auto_splits(plan);
+}
+
+int64_t attn_fwd_split_workspace_bytes(const attn_fwd_plan *plan, int32_t n_splits) {
+    if (!plan || !split_supported(plan)) return -1;
+    if (n_splits <= 0) n_splits = auto_splits(plan);
+    if (n_splits > kMaxSplits) return -1;
+    return split_workspace(plan, n_splits);
+}
+
+attn_status attn_fwd_run_split(const attn_fwd_plan *plan, const void *Q, const void *K, const void *V,
+                               void *O, float *lse, int32_t n_splits, void *workspace,
+                               int64_t workspace_bytes, void *stream) {
+    if (!plan || !Q || !K || !V || !O || !workspace) return ATTN_ERR_INVALID;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(workspace) ||
+        (lse && ((uintptr_t)lse & 3u)))
+        return ATTN_ERR_INVALID;
+    if (!split_supported(plan)) return ATTN_ERR_UNSUPPORTED;
+    if (n_splits <= 0) n_splits = auto_splits(plan);
+    if (n_splits > kMaxSplits) return ATTN_ERR_INVALID;
+    if (workspace_bytes < split_workspace(plan, n_splits)) return ATTN_ERR_INVALID;
+    const KernelArgs a = make_args(plan, Q, K, V, O, lse);
+    hipStream_t s = (hipStream_t)stream;
+    const hipError_t e = plan->variant == V_D128_BF16 ? launch_split<128>(plan, a, n_splits, (float *)workspace, s)
+                                                      : launch_split<64>(plan, a, n_splits, (float *)workspace, s);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 attn_status attn_fwd_plan_info(const attn_fwd_plan *plan, int64_t *grid, int32_t *block,

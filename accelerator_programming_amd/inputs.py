@@ -33,6 +33,7 @@ class Workload:
     k_mult: float = 1.0          # K scaled after the draw (exact in bf16 for 2.0)
     v_from_k: bool = False       # V is the first dv columns of K (a strided view)
     scale: float = field(default=0.0)
+    decode: bool = False         # run through the split-KV path (few query rows)
 
     @property
     def softmax_scale(self) -> float:
@@ -69,7 +70,15 @@ C4 = Workload("C4_B1_Hq32_Hkv8_N16384_d128_causal_K2", 1, 32, 8, 16384, 16384, 1
 C5 = Workload("C5_B1_Hq128_Hkv1_Nq64_Nkv8192_dqk576_dv512", 1, 128, 1, 64, 8192, 576, 512, False,
               torch.bfloat16, 1005, v_from_k=True)
 
-WORKLOADS = {w.name.split("_")[0]: w for w in (C1, C2, C3, C4, C5)}
+# Decode-shaped workloads for the split-KV path (seeds 2001-2002): Llama-3.1-8B
+# attention heads (H_q 32, H_kv 8, d 128) at one new token per sequence over a
+# 32K-key cache (batch 4), and 4 new tokens over a 128K-key cache.
+D1 = Workload("D1_B4_Hq32_Hkv8_Nq1_Nkv32768_d128_decode", 4, 32, 8, 1, 32768, 128, 128, False,
+              torch.bfloat16, 2001, decode=True)
+D2 = Workload("D2_B1_Hq32_Hkv8_Nq4_Nkv131072_d128_decode", 1, 32, 8, 4, 131072, 128, 128, False,
+              torch.bfloat16, 2002, decode=True)
+
+WORKLOADS = {w.name.split("_")[0]: w for w in (C1, C2, C3, C4, C5, D1, D2)}
 
 
 def make_inputs(w: Workload, device: str | torch.device = "cpu"):
@@ -97,6 +106,8 @@ def sample_rows(w: Workload, n: int, seed: int = 7) -> torch.Tensor:
     g.manual_seed(seed)
     fixed = []
     for i in (0, 1, w.Nq - 1, w.Nq // 2):
+        if i >= w.Nq:
+            continue  # one query row: 0 only
         fixed.append((0, 0, i))
         fixed.append((w.B - 1, w.Hq - 1, i))
     m = max(n - len(fixed), 0)

@@ -73,7 +73,8 @@ typedef struct {
  * attn_fwd_destroy). Makes no HIP call. Returns ATTN_ERR_INVALID for
  * non-positive sizes, H_q not a multiple of H_kv, a non-finite or
  * non-positive scale, or plan == NULL; ATTN_ERR_UNSUPPORTED for head
- * dimensions without a kernel (supported: d = 64 and d = 128).
+ * dimensions without a kernel (here d = 64 and d = 128; attn_fwd_create_ex
+ * also takes d = 576 with d_v = 512).
  */
 attn_status attn_fwd_create(attn_fwd_plan **plan, int64_t B, int64_t H_q, int64_t H_kv,
                             int64_t N, int64_t d, int32_t causal, float scale);
@@ -84,7 +85,7 @@ attn_status attn_fwd_create(attn_fwd_plan **plan, int64_t B, int64_t H_q, int64_
  * with N_kv != N, strides that are not 16-byte multiples, row strides below
  * the row width, or a tensor whose [N, d] slab exceeds 2^31 elements.
  * Supported (d, d_v, dtype): (64, 64, bf16), (128, 128, bf16),
- * (64, 64, fp32).
+ * (64, 64, fp32), (576, 512, bf16).
  */
 attn_status attn_fwd_create_ex(const attn_fwd_params *params, attn_fwd_plan **plan);
 
@@ -100,6 +101,49 @@ attn_status attn_fwd_create_ex(const attn_fwd_params *params, attn_fwd_plan **pl
  */
 attn_status attn_fwd_run(const attn_fwd_plan *plan, const void *Q, const void *K,
                          const void *V, void *O, float *lse, void *stream);
+
+/*
+ * Split-KV forward (few query rows per kv head, long key sequences: decode).
+ * The keys of each kv head are cut into n_splits contiguous ranges; each
+ * range's attention of all the group's query rows is computed separately and
+ * written, as O / l (fp32) and its logsumexp, to a caller-provided workspace;
+ * a second kernel merges the ranges exactly: lse = ln Σ_s exp(lse_s),
+ * O = Σ_s exp(lse_s - lse) O_s. The result equals attn_fwd_run's (same
+ * method, "Distilling a 4.5 hour CUDA talk", section 7: the running max and
+ * normalizer carried across key tiles, here also across ranges).
+ * Served problems: the plan's (d, d_v, dtype) is (64, 64, bf16) or
+ * (128, 128, bf16), not causal, and (H_q / H_kv) * N <= 64 (all query rows
+ * of a kv head fit one workgroup).
+ */
+
+/*
+ * attn_fwd_split_count - the number of key ranges the library would use for
+ * the plan (enough workgroups for every CU, at most 64, at least one 64-key
+ * tile each), or 0 if the split path does not serve the plan (or plan is NULL).
+ */
+int32_t attn_fwd_split_count(const attn_fwd_plan *plan);
+
+/*
+ * attn_fwd_split_workspace_bytes - device bytes attn_fwd_run_split needs for
+ * n_splits key ranges (n_splits <= 0: the library's count):
+ * n_splits * B * H_q * N * (d_v + 1) * 4. Returns -1 if the split path does
+ * not serve the plan or n_splits > 64.
+ */
+int64_t attn_fwd_split_workspace_bytes(const attn_fwd_plan *plan, int32_t n_splits);
+
+/*
+ * attn_fwd_run_split - as attn_fwd_run, through n_splits key ranges
+ * (n_splits <= 0: the library's count). workspace is a caller-owned device
+ * buffer of at least attn_fwd_split_workspace_bytes(plan, n_splits) bytes,
+ * 16-byte aligned; its contents on entry do not matter and on return are
+ * scratch. Two kernels are queued on `stream`; calls that share a workspace
+ * must not overlap. Returns ATTN_ERR_INVALID for NULL or misaligned pointers,
+ * n_splits > 64 or a short workspace; ATTN_ERR_UNSUPPORTED if the split path
+ * does not serve the plan; ATTN_ERR_HIP if a launch fails.
+ */
+attn_status attn_fwd_run_split(const attn_fwd_plan *plan, const void *Q, const void *K,
+                               const void *V, void *O, float *lse, int32_t n_splits,
+                               void *workspace, int64_t workspace_bytes, void *stream);
 
 /* attn_fwd_destroy - free a plan. NULL is accepted and ignored. */
 void attn_fwd_destroy(attn_fwd_plan *plan);

@@ -181,3 +181,63 @@ def test_status_strings():
     assert attn.attn_status_str(ATTN_OK) == "ATTN_OK"
     assert attn.attn_status_str(ATTN_ERR_UNSUPPORTED) == "ATTN_ERR_UNSUPPORTED"
     assert attn.attn_status_str(99) == "ATTN_ERR_UNKNOWN"
+
+
+# ---------------------------------------------------------------------------
+# Split-KV entry points: choice, workspace size and argument checks (no launch)
+# ---------------------------------------------------------------------------
+def split_plan(**kw):
+    args = dict(B=1, H_q=32, H_kv=8, N=4, N_kv=4096, d=128, causal=0, scale=1 / math.sqrt(128))
+    args.update(kw)
+    return attn.attn_fwd_create_ex(ex_params(**args))
+
+
+def test_split_count_and_workspace_size():
+    plan = split_plan()
+    try:
+        n = attn.attn_fwd_split_count(plan)
+        assert 1 <= n <= 64
+        rows = 1 * 32 * 4
+        assert attn.attn_fwd_split_workspace_bytes(plan, 0) == n * rows * (128 + 1) * 4
+        assert attn.attn_fwd_split_workspace_bytes(plan, 3) == 3 * rows * (128 + 1) * 4
+        assert attn.attn_fwd_split_workspace_bytes(plan, 65) == -1
+    finally:
+        attn.attn_fwd_destroy(plan)
+    # at most one split per 64-key tile
+    plan = split_plan(N_kv=100)
+    try:
+        assert attn.attn_fwd_split_count(plan) == 2
+    finally:
+        attn.attn_fwd_destroy(plan)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(causal=1, N=4096),                      # causal
+    dict(N=32),                                  # 4 x 32 = 128 query rows per kv head
+    dict(d=576, d_v=512, H_q=128, H_kv=1, N=1),  # wide heads
+], ids=["causal", "too_many_rows", "wide"])
+def test_split_path_declines_unserved_plans(kw):
+    plan = split_plan(**kw)
+    try:
+        assert attn.attn_fwd_split_count(plan) == 0
+        assert attn.attn_fwd_split_workspace_bytes(plan, 0) == -1
+        L = attn.lib()
+        assert L.attn_fwd_run_split(plan, 16, 16, 16, 16, None, 0, 16, 1 << 30, None) == \
+            ATTN_ERR_UNSUPPORTED
+    finally:
+        attn.attn_fwd_destroy(plan)
+
+
+def test_run_split_rejects_bad_arguments_before_launch():
+    plan = split_plan()
+    try:
+        L = attn.lib()
+        need = attn.attn_fwd_split_workspace_bytes(plan, 0)
+        assert L.attn_fwd_run_split(None, 16, 16, 16, 16, None, 0, 16, need, None) == ATTN_ERR_INVALID
+        assert L.attn_fwd_run_split(plan, 16, 16, 16, 16, None, 0, None, need, None) == ATTN_ERR_INVALID
+        assert L.attn_fwd_run_split(plan, 16, 16, 16, 16, None, 0, 24, need, None) == ATTN_ERR_INVALID
+        assert L.attn_fwd_run_split(plan, 16, 16, 16, 16, None, 0, 16, need - 4, None) == ATTN_ERR_INVALID
+        assert L.attn_fwd_run_split(plan, 16, 16, 16, 16, None, 65, 16, 1 << 40, None) == ATTN_ERR_INVALID
+        assert L.attn_fwd_run_split(plan, 16 + 2, 16, 16, 16, None, 0, 16, need, None) == ATTN_ERR_INVALID
+    finally:
+        attn.attn_fwd_destroy(plan)

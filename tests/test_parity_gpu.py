@@ -204,3 +204,59 @@ def test_repeat_runs_are_bitwise_identical():
     o2, l2 = run_gpu(q, k, v, True, w.softmax_scale)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ---------------------------------------------------------------------------
+# Split-KV path (decode-shaped problems): same oracle, same tolerances
+# ---------------------------------------------------------------------------
+SPLIT = [
+    # B, Hq, Hkv, Nq, Nkv, d, n_splits (0: the library's count)
+    (1, 32, 8, 1, 4096, 128, 0),
+    (2, 8, 2, 4, 1000, 64, 3),       # ragged last range and tile
+    (1, 16, 1, 4, 8192, 128, 0),     # 64 query rows per kv head (the limit)
+    (1, 4, 4, 1, 65, 128, 2),        # a one-key last range
+    (1, 8, 8, 2, 100, 128, 8),       # more ranges than tiles: empty ranges
+    (3, 6, 3, 3, 777, 64, 1),        # one range
+]
+
+
+def run_split(q, k, v, scale, n_splits):
+    B, Hq, N, _ = q.shape
+    o = torch.empty((B, Hq, N, v.shape[3]), dtype=q.dtype, device="cuda")
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device="cuda")
+    op = attn.AttnFwd(q, k, v, False, scale, o)
+    try:
+        assert op.split_count() >= 1
+        op.run_split(q, k, v, o, lse, n_splits=n_splits)
+    finally:
+        op.close()
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("shape", SPLIT, ids=lambda s: "B%d_Hq%d_Hkv%d_Nq%d_Nkv%d_d%d_s%d" % s)
+def test_split_kv_shapes(shape):
+    B, Hq, Hkv, Nq, Nkv, d, ns = shape
+    w = Workload("split", B, Hq, Hkv, Nq, Nkv, d, d, False, torch.bfloat16, 77 + Nkv + Nq)
+    q, k, v = make_inputs(w, "cuda")
+    o, lse = run_split(q, k, v, w.softmax_scale, ns)
+    compare(o, lse, q, k, v, False, w.softmax_scale)
+
+
+def test_split_kv_equals_single_pass_within_tolerance():
+    w = Workload("split_vs_full", 1, 8, 2, 8, 2048, 128, 128, False, torch.bfloat16, 4242)
+    q, k, v = make_inputs(w, "cuda")
+    o1, l1 = run_split(q, k, v, w.softmax_scale, 0)
+    o2, l2 = run_gpu(q, k, v, False, w.softmax_scale)
+    torch.cuda.synchronize()
+    assert (o1.float() - o2.float()).abs().max().item() <= TOL_O
+    assert (l1 - l2).abs().max().item() <= TOL_LSE
+
+
+@pytest.mark.parametrize("name", ["D1", "D2"])
+def test_decode_workloads_full_size_sampled(name):
+    from accelerator_programming_amd.inputs import WORKLOADS
+    w = WORKLOADS[name]
+    q, k, v = make_inputs(w, "cuda")
+    o, lse = run_split(q, k, v, w.softmax_scale, 0)
+    compare(o, lse, q, k, v, False, w.softmax_scale, rows=sample_rows(w, 128))
