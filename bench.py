@@ -26,6 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12  # 2516.6
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 PROFILES = os.path.join(ROOT, "profiles")
 METRIC = "attention fwd TFLOP/s on 1 MI355X + % of bf16 MFMA peak (causal FLOPs /2)"
 
@@ -43,6 +44,8 @@ def kernel_source_sha() -> str:
 def kernel_name(w):
     """The kernel the library launches for workload w (as rocprofv3 names it)."""
     causal = "true" if w.causal else "false"
+    if w.decode:
+        return "attn::attn_split_kernel<%d> + attn::attn_split_merge<%d>" % (w.dqk, w.dqk)
     if w.dqk == 576:
         # V given as the leading columns of K takes the kernel that stages K only
         return "attn::attn_fwd_wide_%skernel<576, 512, %s>" % ("vk_" if w.v_from_k else "", causal)
@@ -141,6 +144,11 @@ def main() -> int:
     o = torch.empty((B, Hq, N, w.dv), dtype=q.dtype, device="cuda")
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device="cuda")
     op = attn.AttnFwd(q, k, v, w.causal, w.softmax_scale, o)
+    if w.decode:
+        # split-KV path; its workspace is allocated here, outside the timed steps
+        ws = torch.empty(attn.attn_fwd_split_workspace_bytes(op.plan, 0), dtype=torch.uint8,
+                         device="cuda")
+        op.run = lambda q, k, v, o, lse, stream=None: op.run_split(q, k, v, o, lse, 0, ws, stream)
     stream = torch.cuda.current_stream()
 
     for _ in range(args.warmup):
@@ -165,6 +173,7 @@ def main() -> int:
     flops = w.flops()
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (kern_avg_ms * 1e-3) / 1e12
+    gbs = w.io_bytes() / (kern_avg_ms * 1e-3) / 1e9  # algorithmic bytes (each tensor once)
     finite = bool(torch.isfinite(o).all().item() and torch.isfinite(lse).all().item())
 
     cpu = None
@@ -190,12 +199,18 @@ def main() -> int:
                    "gflop_per_step": round(flops / 1e9, 3), "parallelism": "single-gpu",
                    "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
                    "outputs_finite": finite},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
-                     "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_for_current_kernel(w.name, args.config),
-                     "kernel_ms_avg": round(kern_avg_ms, 4),
-                     "kernel": kernel_name(w)},
+        "roofline": ({"bound": "mfma", "achieved": round(achieved, 2),
+                      "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
+                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                      "traffic": traffic_for_current_kernel(w.name, args.config),
+                      "kernel_ms_avg": round(kern_avg_ms, 4),
+                      "kernel": kernel_name(w)} if not w.decode else
+                     {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                      "traffic": traffic_for_current_kernel(w.name, args.config),
+                      "kernel_ms_avg": round(kern_avg_ms, 4),
+                      "tflops": round(achieved, 2),
+                      "kernel": kernel_name(w)}),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
