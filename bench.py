@@ -57,7 +57,7 @@ def traffic_for_current_kernel(workload_name: str, tag: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None when it was taken on other kernel sources or another workload."""
     try:
-        with open(os.path.join(PROFILES, "attn_fwd_%s_traffic.json" % tag)) as f:
+        with open(os.path.join(PROFILES, "%s_traffic.json" % tag)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -202,12 +202,12 @@ def main() -> int:
         "roofline": ({"bound": "mfma", "achieved": round(achieved, 2),
                       "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
                       "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                      "traffic": traffic_for_current_kernel(w.name, args.config),
+                      "traffic": traffic_for_current_kernel(w.name, "attn_fwd_" + args.config),
                       "kernel_ms_avg": round(kern_avg_ms, 4),
                       "kernel": kernel_name(w)} if not w.decode else
                      {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                       "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                      "traffic": traffic_for_current_kernel(w.name, args.config),
+                      "traffic": traffic_for_current_kernel(w.name, "attn_split_" + args.config),
                       "kernel_ms_avg": round(kern_avg_ms, 4),
                       "tflops": round(achieved, 2),
                       "kernel": kernel_name(w)}),
