@@ -9,29 +9,29 @@
 // a per-row reference and a normalizer.
 //
 // gfx950 mapping
-//  * 8 waves, two per SIMD. Waves p and p + 4 form a pair on SIMD p and share
-//    query rows q0 + 64p .. q0 + 64p + 63 (two 32-row blocks). In each 64-key
-//    tile, role r = 0 / 1 (wave p / p + 4) scores keys 32r .. 32r + 31 and
-//    accumulates O columns 64r .. 64r + 63 (d = 128; half of d in general).
-//    Every K or V fragment read from LDS feeds the MFMAs of both row blocks.
-//  * Why pairs: on gfx950 a wave's VALU work does not overlap its own MFMAs,
-//    while VALU and MFMA work of two waves on one SIMD do overlap. The two
-//    roles run their period in different orders (role 0: P·V, scores,
-//    softmax; role 1: scores, softmax, P·V), so each one's exponentials run
-//    while the other's MFMAs execute: compute never idle, as the pages ask
-//    ("CS149 L11: Programming Specialized Hardware", section 4, slide 35),
-//    with the producer / consumer split of "Distilling a 4.5 hour CUDA talk",
-//    section 12, becoming a score / value split between two waves.
+//  * 8 waves, two per SIMD (waves p and p + 4 share SIMD p). Wave w owns the
+//    32 query rows q0 + 32w .. q0 + 32w + 31 over every key and every output
+//    column, so a wave's softmax, P and O never leave its registers; the
+//    waves share only the K/V tiles in LDS.
+//  * Why two phase orders: on gfx950 a wave's VALU work does not overlap its
+//    own MFMAs, while the VALU and MFMA work of two waves on one SIMD do. In
+//    each period (one 64-key tile) wave p (role 0) runs its MFMAs first, P·V
+//    of the previous tile and the scores of this one, then its softmax; wave
+//    p + 4 (role 1) runs its softmax first, on scores it computed at the end
+//    of the previous period, then P·V and the next tile's scores. Each wave's
+//    exponentials run while its SIMD partner's MFMAs execute: compute never
+//    idle, as the pages ask ("CS149 L11: Programming Specialized Hardware",
+//    section 4, slide 35), the two-group alternation that "Distilling a 4.5
+//    hour CUDA talk", section 12, describes for its consumers.
 //  * Scores are computed transposed, Sᵀ = K·Qᵀ, with 32x32x16 bf16 MFMAs:
-//    A = a 32-key slab of K read from LDS, B = the block's Q fragment held in
+//    A = a 32-key slab of K read from LDS, B = the wave's Q fragment held in
 //    VGPRs for the whole loop. In the accumulator every lane holds one query
 //    row (l % 32) and 16 keys, so the softmax row work is in-lane.
 //  * Oᵀ += Vᵀ·Pᵀ: Pᵀ is the score accumulator converted to bf16 in place. The
 //    keys a lane holds come in runs of four (rows 8*(r/4) + 4g + r%4), so the
 //    MFMA k index 8g + e names key 8*(e/4) + 4g + e%4 of each 16-key chunk.
 //    The Vᵀ operand is read from the row-major V tile with the LDS transpose
-//    read (ds_read_b64_tr_b16) in exactly that key order. Each role writes its
-//    P to LDS in register order; both roles read both halves back.
+//    read (ds_read_b64_tr_b16) in exactly that key order.
 //  * Softmax in base 2 with log2(e) folded into the scale on the host, and
 //    one reciprocal per row at the end ("Distilling a 4.5 hour CUDA talk",
 //    section 2 on the base-2 exponential and on reciprocal reuse; section 7
@@ -40,13 +40,20 @@
 //    exact in real arithmetic for any m, so nothing is rescaled in the loop.
 //    If some row's l leaves [0, 2^32] (a later key outscored the first ones by
 //    a wide margin) the workgroup recomputes with exact row maxima.
-//  * K/V staging: role-1 waves are also the loaders: they issue LDS-DMA
-//    (global_load_lds_dwordx4, no VGPRs) for K(T+1) and V(T) at the start of
-//    period T into two-stage rings; "my loads landed" (s_waitcnt vmcnt(0))
-//    plus one barrier close each period. LDS-DMA writes 16 bytes per lane at
-//    consecutive addresses, so bank-conflict avoidance is an XOR swizzle of the
-//    16-byte chunks of a row, applied by choosing which global chunk each lane
-//    fetches ("Distilling a 4.5 hour CUDA talk", section 8).
+//  * K/V staging: four-stage rings of K and of V, filled by LDS-DMA
+//    (buffer_load ... lds, no VGPRs). Two copy groups (the four role-0 waves,
+//    the four role-1 waves) take turns: in period T the group T % 2 copies
+//    K(T+3) and V(T+2), one LDS-DMA after every fourth MFMA of its two MFMA
+//    chains (the copy engine accepts them at about that pace; a burst would
+//    stall the issuing wave), and waits for them (s_waitcnt vmcnt(0)) at the
+//    end of period T+1. One barrier closes each period. LDS-DMA writes 16
+//    bytes per lane at consecutive addresses, so bank-conflict avoidance is
+//    an XOR swizzle of the 16-byte chunks of a row, applied by choosing which
+//    global chunk each lane fetches ("Distilling a 4.5 hour CUDA talk",
+//    section 8).
+//  * Causal: a wave stops computing after the last tile any of its rows
+//    sees and only keeps its copy duty and the barriers until the
+//    workgroup's last period.
 #pragma once
 #include <type_traits>
 
@@ -68,22 +75,24 @@ struct KernelArgs {
 
 template <int D>
 struct TileCfg {
-    static constexpr int TQ = 256;          // query rows per workgroup
-    static constexpr int TK = 64;           // keys per tile (one 32-key half per role)
+    static constexpr int TQ = 256;           // query rows per workgroup
+    static constexpr int TK = 64;            // keys per tile
     static constexpr int NWAVE = 8;
-    static constexpr int NT = 64 * NWAVE;   // threads per workgroup
-    static constexpr int CPR = D / 8;       // 16-byte chunks per K or V row
-    static constexpr int TILE = TK * D;     // elements of one K or V tile
-    static constexpr int P_BYTES = 4096;    // one wave's P: 64 rows x 32 keys bf16
-    static constexpr int P_SLOT = NWAVE * P_BYTES;
-    static constexpr int KV_BYTES = 4 * TILE * 2;  // two K stages, two V stages
-    static constexpr int LDS_BYTES = KV_BYTES + 2 * P_SLOT;
+    static constexpr int ROWS = TQ / NWAVE;  // query rows per wave
+    static constexpr int NT = 64 * NWAVE;    // threads per workgroup
+    static constexpr int CPR = D / 8;        // 16-byte chunks per K or V row
+    static constexpr int TILE = TK * D;      // elements of one K or V tile
+    static constexpr int NSTAGE = 4;         // depth of the K ring and of the V ring
+    static constexpr int LDS_BYTES = 2 * NSTAGE * TILE * 2;
     static constexpr int ROWS_PER_DMA = 64 / CPR;                 // rows per wave-wide DMA
-    static constexpr int DMA_PER_LOADER = TK / ROWS_PER_DMA / 4;  // per tile, tensor and loader wave
-    static constexpr int NKC = D / 16;      // k-steps of Sᵀ = K·Qᵀ
-    static constexpr int NDB = D / 64;      // 32-column blocks of O per role
-    static_assert(TK % (ROWS_PER_DMA * 4) == 0, "tile rows must split over the loader waves");
-    static_assert(D % 64 == 0, "each role owns a multiple of 32 output columns");
+    static constexpr int DMA_PER_COPIER = TK / ROWS_PER_DMA / 4;  // per tile, tensor and copying wave
+    static constexpr int NKC = D / 16;       // k-steps of Sᵀ = K·Qᵀ
+    static constexpr int NDB = D / 32;       // 32-column blocks of O
+    static_assert(ROWS == 32, "one 32-row MFMA block per wave");
+    static_assert(TK % (ROWS_PER_DMA * 4) == 0, "tile rows must split over a copy group");
+    static_assert(LDS_BYTES <= 160 * 1024, "the rings must fit in LDS");
+    static_assert(4 * DMA_PER_COPIER == 4 * NDB && 4 * DMA_PER_COPIER == 2 * NKC,
+                  "one copy per four MFMAs of each chain");
 };
 
 template <int N>
@@ -95,16 +104,16 @@ attn_fwd_kernel(const KernelArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
     using C = TileCfg<D>;
     constexpr int TQ = C::TQ, TK = C::TK, CPR = C::CPR, NKC = C::NKC, NDB = C::NDB;
-    constexpr int DPL = C::DMA_PER_LOADER;
+    constexpr int NS = C::NSTAGE, DPC = C::DMA_PER_COPIER;
     __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[C::LDS_BYTES];
-    __bf16 *const Kst = (__bf16 *)lds_raw;             // two K stages
-    __bf16 *const Vst = Kst + 2 * C::TILE;             // two V stages
-    unsigned char *const Pst = lds_raw + C::KV_BYTES;  // two P slots
+    __shared__ int wave_bad[C::NWAVE];
+    __bf16 *const Kst = (__bf16 *)lds_raw;   // K ring
+    __bf16 *const Vst = Kst + NS * C::TILE;  // V ring
 
     const int tid = threadIdx.x;
     int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int pair = w & 3, role = w >> 2;
+    const int role = w >> 2, cw = w & 3;  // cw: this wave's share of its group's copies
     int l32 = lane & 31, g = lane >> 5;
 
     // ---- work item: heaviest causal tiles are dispatched first. Workgroups
@@ -139,71 +148,80 @@ attn_fwd_kernel(const KernelArgs a) {
     TIn *__restrict__ Op = (TIn *)a.o + b * a.o_sb + h * a.o_sh;
 
     const int q0 = qt * TQ;
-    const int prow0 = q0 + 64 * pair;  // first query row of this pair
+    const int wrow0 = q0 + C::ROWS * w;  // first query row of this wave
+    const int row = wrow0 + l32;         // the query row of this lane
     const int kv_end = CAUSAL ? min(a.Nkv, q0 + TQ) : a.Nkv;
-    const int n_tiles = (kv_end + TK - 1) / TK;  // >= 1
-    // 32-key half-tiles from this index on need the causal or key-range mask;
-    // tiles below n_plain have none
-    const int first_masked_sub = CAUSAL ? min(q0 / 32, a.Nkv / 32) : a.Nkv / 32;
+    const int n_tiles = (kv_end + TK - 1) / TK;  // >= 1; the workgroup's periods
+    // tiles this wave computes: under the causal mask, tiles past its last
+    // row hold no key any of its rows sees
+    const int n_live = CAUSAL ? min(n_tiles, (wrow0 + C::ROWS - 1) / TK + 1) : n_tiles;
+    // 32-key halves from this index on need the causal or key-range mask for
+    // this wave's rows; tiles below n_plain have none
+    const int first_masked_sub = CAUSAL ? min(wrow0 / 32, a.Nkv / 32) : a.Nkv / 32;
     const int n_plain = min(n_tiles, first_masked_sub / 2);
 
-    // ---- Q fragments: B operands of Sᵀ = K·Qᵀ, resident for the whole loop --
-    bf16x8 qf[2][NKC];
+    // ---- Q fragment: B operand of Sᵀ = K·Qᵀ, resident for the whole loop ---
+    bf16x8 qf[NKC];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        const int row = prow0 + 32 * rb + l32;
-#pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) {
-            u32x4 v = {0, 0, 0, 0};
-            if (row < a.Nq) v = load8_bf16(Qp + (int64_t)row * a.q_sn + 16 * kc + 8 * g);
-            qf[rb][kc] = u32x4_as_bf16x8(v);
-        }
+    for (int kc = 0; kc < NKC; ++kc) {
+        u32x4 v = {0, 0, 0, 0};
+        if (row < a.Nq) v = load8_bf16(Qp + (int64_t)row * a.q_sn + 16 * kc + 8 * g);
+        qf[kc] = u32x4_as_bf16x8(v);
     }
 
-    // ---- LDS stages; PAR is the tile index parity (a compile-time constant
-    // in the unrolled loop, so stage offsets are instruction immediates) ----
-    auto kstage = [&](auto PAR) __attribute__((always_inline)) {
-        return Kst + decltype(PAR)::value * C::TILE;
+    // ---- ring stages; S is a compile-time constant in the unrolled loop, so
+    // stage offsets are instruction immediates ---------------------------------
+    auto kst = [&](auto S) __attribute__((always_inline)) { return Kst + decltype(S)::value * C::TILE; };
+    auto vst = [&](auto S) __attribute__((always_inline)) { return Vst + decltype(S)::value * C::TILE; };
+    auto lds_barrier = [&]() __attribute__((always_inline)) {
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     };
-    auto vstage = [&](auto PAR) __attribute__((always_inline)) {
-        return Vst + decltype(PAR)::value * C::TILE;
-    };
-    // P of wave (pair, rl) for a tile of parity PAR, in register order:
-    // 16-byte chunk j of lane l at byte 16 * (64 j + l), conflict-free
-    auto pslot = [&](auto PAR, int rl) __attribute__((always_inline)) {
-        return Pst + decltype(PAR)::value * C::P_SLOT + (pair + 4 * rl) * C::P_BYTES;
+    auto wait_copies = [&]() __attribute__((always_inline)) {
+        // a partial vmcnt does not order LDS-DMA writes; only zero is used
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     };
 
-    // ---- LDS-DMA of one K or V tile by the four loader (role-1) waves. A
-    // window is 64 lanes x 16 bytes = ROWS_PER_DMA rows; loader `pair` fills
-    // windows pair, pair + 4, ...; lane i of a window lands at chunk i and
-    // fetches the global chunk that the swizzle puts there. bf16 inputs go
-    // through a buffer resource that ends at the last key, so rows past the
-    // end read as zeros (finite, and masked). -----------------------------
+    // ---- LDS-DMA of one K or V tile by one copy group. A window is 64 lanes
+    // x 16 bytes = ROWS_PER_DMA rows; the group's wave cw fills windows cw,
+    // cw + 4, ...; lane i of a window lands at chunk i and fetches the global
+    // chunk that the swizzle puts there. bf16 inputs go through a buffer
+    // resource that ends at the last key, so rows past the end read as zeros
+    // (finite, and masked). ---------------------------------------------------
     int dma_r = lane / CPR;  // row within the window
     int dma_p = lane % CPR;  // physical chunk this lane fills
-    auto issue = [&](auto PAR, bool is_v, int tile) __attribute__((always_inline)) {
-        __bf16 *dst = is_v ? vstage(PAR) : kstage(PAR);
+    // this lane's byte offset, within a tile, of window u of its share
+    // (bf16 inputs); formed once per pass, like the LDS read addresses
+    uint32_t voff_k[DPC], voff_v[DPC];
+    auto form_copy_offsets = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < DPC; ++u) {
+            const uint32_t r = (4 * u + cw) * C::ROWS_PER_DMA + dma_r;  // tile row
+            voff_k[u] = (r * (uint32_t)a.k_sn + 8u * k_chunk<D>(r, dma_p)) * 2u;
+            voff_v[u] = (r * (uint32_t)a.v_sn + 8u * v_chunk<D>(r, dma_p)) * 2u;
+            asm volatile("" : "+v"(voff_k[u]), "+v"(voff_v[u]));
+        }
+    };
+    // window u (0 .. DPC-1) of this wave's share of one tile
+    auto issue_one = [&](__bf16 *dst, bool is_v, int tile, int u) __attribute__((always_inline)) {
         const TIn *base = is_v ? Vp : Kp;
         const int32_t sn = is_v ? a.v_sn : a.k_sn;
         if constexpr (sizeof(TIn) == 2) {
-            const int rem = a.Nkv - tile * TK;  // keys left, >= 1
-            const uint32_t bytes = (uint32_t)(((int64_t)(rem - 1) * sn + D) * 2);
+            // the resource covers the rows of this tile that exist; a row
+            // past the last key starts at or beyond its end (the row stride
+            // is at least D; should the offset wrap, it names an existing
+            // row, whose values are finite and masked). A tile past the last
+            // one gets an empty resource: its copy writes zeros to the
+            // (free) stage and reads nothing.
+            const int rows = max(0, min(a.Nkv - tile * TK, TK));
+            // wave-uniform; kept in an SGPR for the resource
+            const uint32_t bytes = __builtin_amdgcn_readfirstlane(
+                rows > 0 ? ((uint32_t)(rows - 1) * (uint32_t)sn + D) * 2u : 0u);
             const u32x4 rsrc = buffer_rsrc(base + (int64_t)tile * TK * sn, bytes);
-#pragma unroll
-            for (int u = 0; u < DPL; ++u) {
-                const int win_id = 4 * u + pair;
-                const int r = win_id * C::ROWS_PER_DMA + dma_r;  // tile row
-                const int chunk = is_v ? v_chunk<D>(r, dma_p) : k_chunk<D>(r, dma_p);
-                const int64_t off = ((int64_t)r * sn + 8 * chunk) * 2;
-                const uint32_t voff = off < (int64_t)bytes ? (uint32_t)off : 0xFFFFFFF0u;
-                dma16_buf_to_lds(rsrc, voff, dst + win_id * 64 * 8);
-            }
+            dma16_buf_to_lds(rsrc, is_v ? voff_v[u] : voff_k[u], dst + (4 * u + cw) * 64 * 8);
         } else {
             // fp32 inputs: rounded to bf16 in registers, same LDS placement
-#pragma unroll
-            for (int u = 0; u < DPL; ++u) {
-                const int win_id = 4 * u + pair;
+            {
+                const int win_id = 4 * u + cw;
                 const int r = win_id * C::ROWS_PER_DMA + dma_r;
                 const int key = min(tile * TK + r, a.Nkv - 1);  // clamped: a finite, masked row
                 const int chunk = is_v ? v_chunk<D>(r, dma_p) : k_chunk<D>(r, dma_p);
@@ -212,128 +230,127 @@ attn_fwd_kernel(const KernelArgs a) {
             }
         }
     };
+    auto issue = [&](__bf16 *dst, bool is_v, int tile) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < DPC; ++u) issue_one(dst, is_v, tile, u);
+    };
 
     // ---- state -------------------------------------------------------------
-    f32x16 oacc[2][NDB];  // O columns 32 * (NDB * role + db) .. of both row blocks
-    float m[2] = {0.f, 0.f};  // per-row reference of the exponentials (score*c units)
-    float l[2];               // normalizer, partial over this wave's keys and lane half
+    f32x16 oacc[NDB];  // Oᵀ: columns 32db + acc_row(r, g) of this lane's row
+    float m = 0.f;     // the row's reference of the exponentials (score*c units)
+    float l = 0.f;     // normalizer, partial over this lane's keys
 
-    // Sᵀ of one 32-key half-tile (rows kq_row0.. of K stage Kq), both row blocks
-    auto scores = [&](f32x16 (&sacc)[2], const __bf16 *Kq, int kq_row0)
-                      __attribute__((always_inline)) {
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[rb][r] = 0.f;
-        bf16x8 kf[NKC];
-        kf[0] = k_frag<D>(Kq, kq_row0 + l32, 0, g);
-        kf[1] = k_frag<D>(Kq, kq_row0 + l32, 1, g);
+    // LDS byte addresses of this lane's fragment reads in stage 0: K rows
+    // l32 (and 32 + l32 at +32 rows) for each k-step, V transpose reads for
+    // each column block. They are made opaque where they are formed (inside
+    // the role branch), so that the compiler keeps these NKC + NDB registers
+    // and puts every stage / row / key-chunk offset in the instruction's
+    // 16-bit immediate instead of materialising an address per offset (the
+    // V ring lies beyond 64 KiB).
+    uint32_t kaddr[NKC], vaddr[NDB];
+    auto form_addresses = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc) {
-            if (kc + 2 < NKC) kf[kc + 2] = k_frag<D>(Kq, kq_row0 + l32, kc + 2, g);
+            kaddr[kc] = lds_addr(&k_frag_ptr<D>(Kst, l32, 2 * kc + g));
+            asm volatile("" : "+v"(kaddr[kc]));
+        }
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) sacc[rb] = mfma_32x32x16(kf[kc], qf[rb][kc], sacc[rb]);
+        for (int db = 0; db < NDB; ++db) {
+            vaddr[db] = lds_addr(vt_read_ptr<D>(Vst, db, lane));
+            asm volatile("" : "+v"(vaddr[db]));
+        }
+    };
+
+    auto no_hook = [](int) {};
+    // Sᵀ of one 64-key tile (K stage S): s[js] holds keys 32js .. 32js + 31
+    auto scores = [&](f32x16 (&s)[2], auto S, auto hook) __attribute__((always_inline)) {
+        constexpr uint32_t so = decltype(S)::value * C::TILE * 2;
+#pragma unroll
+        for (int js = 0; js < 2; ++js)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[js][r] = 0.f;
+        constexpr int NF = 2 * NKC;  // fragment f: k-step f / 2 of half f % 2
+        bf16x8 kf[NF];
+        auto kread = [&](int f) __attribute__((always_inline)) {
+            return lds_read_b128(kaddr[f >> 1] + so + (f & 1) * 32 * D * 2);
+        };
+        kf[0] = kread(0);
+        kf[1] = kread(1);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            if (f + 2 < NF) kf[f + 2] = kread(f + 2);
+            s[f & 1] = mfma_32x32x16(kf[f], qf[f >> 1], s[f & 1]);
             // a scheduling boundary: keeps the fragment reads two steps ahead
             // rather than all hoisted (registers are the limit in this kernel)
             asm volatile("" ::);
+            hook(f);
         }
     };
-    // scores of half-tile js as floats, with the causal / key-range mask
-    auto masked_scores = [&](bool masked, const f32x16 (&sacc)[2], float (&sv)[2][16], int js)
-                             __attribute__((always_inline)) {
+    // the causal / key-range mask on the scores of tile T
+    auto mask = [&](f32x16 (&s)[2], int T) __attribute__((always_inline)) {
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+        for (int js = 0; js < 2; ++js)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sv[rb][r] = sacc[rb][r];
-        if (masked) {
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-                const int row = prow0 + 32 * rb + l32;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = 32 * js + acc_row(r, g);
-                    if ((CAUSAL && key > row) || key >= a.Nkv) sv[rb][r] = -INFINITY;
-                }
+            for (int r = 0; r < 16; ++r) {
+                const int key = TK * T + 32 * js + acc_row(r, g);
+                if ((CAUSAL && key > row) || key >= a.Nkv) s[js][r] = -INFINITY;
             }
-        }
     };
-    // row maxima of score * c over a half-tile (both wave halves)
-    auto row_max = [&](const float (&sv)[2][16], float (&mx)[2]) __attribute__((always_inline)) {
+    // m from the row's first 32 keys (tile 0, masked)
+    auto fix_m = [&](f32x16 (&s)[2]) __attribute__((always_inline)) {
+        mask(s, 0);
+        float x = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-            float x = fmaxf(sv[rb][0], sv[rb][1]);
-#pragma unroll
-            for (int r = 2; r < 16; r += 2) x = fmaxf(x, fmaxf(sv[rb][r], sv[rb][r + 1]));
-            mx[rb] = xhalf_max(x) * a.c;
-        }
+        for (int r = 2; r < 16; r += 2) x = fmaxf(x, fmaxf(s[0][r], s[0][r + 1]));
+        x = xhalf_max(x) * a.c;
+        m = (x == -INFINITY) ? 0.f : x;
     };
-    // this wave's half of tile T: scores, p = 2^(s·c - m) (Map(exp)), the
-    // partial row sums (Reduce(+)), P to LDS
-    auto score_softmax = [&](auto ROLE, auto PAR, int T, bool masked) __attribute__((always_inline)) {
-        constexpr int R = decltype(ROLE)::value;
-        f32x16 sacc[2];
-        scores(sacc, kstage(PAR), 32 * R);
-        float sv[2][16];
-        masked_scores(masked, sacc, sv, 2 * T + R);
-        // p = 2^(s·c - m) rounded to bf16; the row sums add the rounded p
-        // (what P·V multiplies) two at a time with v_dot2_f32_bf16, in
-        // independent partial sums so no instruction waits on the previous
-        uint32_t pk[2][8];
+    // p = 2^(s·c - m) (Map(exp)) rounded to bf16 into pk, and the partial row
+    // sum of the rounded p (what P·V multiplies; Reduce(+)), two at a time
+    // with v_dot2_f32_bf16 in independent partial sums
+    auto softmax = [&](f32x16 (&s)[2], uint32_t (&pk)[2][8], int T, bool masked)
+                       __attribute__((always_inline)) {
+        if (masked) mask(s, T);
+        const float negm = -m;
+        float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-            const float negm = -m[rb];
+        for (int js = 0; js < 2; ++js) {
             float e[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) e[r] = exp2_hw(__builtin_fmaf(sv[rb][r], a.c, negm));
+            for (int r = 0; r < 16; ++r) e[r] = exp2_hw(__builtin_fmaf(s[js][r], a.c, negm));
 #pragma unroll
-            for (int j = 0; j < 8; ++j) pk[rb][j] = pack_bf16x2(e[2 * j], e[2 * j + 1]);
-            float ls[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < 8; ++j) pk[js][j] = pack_bf16x2(e[2 * j], e[2 * j + 1]);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) ls[j & 3] = sum_bf16x2(pk[rb][j], ls[j & 3]);
-            l[rb] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+            for (int j = 0; j < 8; ++j) ls[j & 3] = sum_bf16x2(pk[js][j], ls[j & 3]);
         }
-        unsigned char *dst = pslot(PAR, R);
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-                *(u32x4 *)(dst + 16 * (64 * (2 * rb + hh) + lane)) =
-                    u32x4{pk[rb][4 * hh], pk[rb][4 * hh + 1], pk[rb][4 * hh + 2], pk[rb][4 * hh + 3]};
+        l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
     };
-    // O (own columns) += P·V for the tile of parity PAR, P of both roles read
-    // back from LDS
-    auto pv = [&](auto ROLE, auto PAR) __attribute__((always_inline)) {
-        constexpr int R = decltype(ROLE)::value;
-        const __bf16 *Vs = vstage(PAR);
-        bf16x8 pf[2][4];  // [rb][16-key chunk of the tile]
+    // Oᵀ += Vᵀ·Pᵀ over one tile (V stage at byte offset so); the 16-key chunk
+    // kch of Pᵀ is pk[kch / 2][4 (kch % 2) .. + 3]
+    // hook(f) runs after MFMA f (the copies issued between them)
+    auto pv = [&](const uint32_t (&pk)[2][8], uint32_t so, auto hook) __attribute__((always_inline)) {
+        constexpr int NF = 4 * NDB;  // fragment f: key chunk f / NDB, column block f % NDB
+        bf16x8 vf[NF];
+        auto vread = [&](int f) __attribute__((always_inline)) {
+            return vt_frag_at<D>(vaddr[f % NDB] + so, f / NDB);
+        };
+        vf[0] = vread(0);
+        vf[1] = vread(1);
 #pragma unroll
-        for (int rl = 0; rl < 2; ++rl) {
-            const unsigned char *src = pslot(PAR, rl);
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh)
-                    pf[rb][2 * rl + hh] = *(const bf16x8 *)(src + 16 * (64 * (2 * rb + hh) + lane));
-        }
-        constexpr int NFV = 4 * NDB;  // Vᵀ fragments: 4 key chunks x NDB column blocks
-        bf16x8 vf[NFV];
-        vf[0] = vt_frag<D>(Vs, NDB * R + 0 % NDB, 0 / NDB, lane);
-        vf[1] = vt_frag<D>(Vs, NDB * R + 1 % NDB, 1 / NDB, lane);
-#pragma unroll
-        for (int f = 0; f < NFV; ++f) {
-            if (f + 2 < NFV) vf[f + 2] = vt_frag<D>(Vs, NDB * R + (f + 2) % NDB, (f + 2) / NDB, lane);
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-                oacc[rb][f % NDB] = mfma_32x32x16(vf[f], pf[rb][f / NDB], oacc[rb][f % NDB]);
+        for (int f = 0; f < NF; ++f) {
+            if (f + 2 < NF) vf[f + 2] = vread(f + 2);
+            const int kch = f / NDB;
+            const u32x4 p = {pk[kch >> 1][4 * (kch & 1)], pk[kch >> 1][4 * (kch & 1) + 1],
+                             pk[kch >> 1][4 * (kch & 1) + 2], pk[kch >> 1][4 * (kch & 1) + 3]};
+            oacc[f % NDB] = mfma_32x32x16(vf[f], u32x4_as_bf16x8(p), oacc[f % NDB]);
             asm volatile("" ::);
+            hook(f);
         }
     };
 
     // ---- one pass over the keys: O, l for the references m ------------------
-    // With set_m, m is first fixed from each row's first 32 keys (both roles
-    // compute the same value); otherwise m already holds the exact row maxima.
-    // Period T: the loaders bring K(T+1) and V(T); role 0 runs P·V(T-1), then
-    // its half of tile T; role 1 its half of tile T, then P·V(T-1).
+    // With set_m, m is first fixed from each row's first 32 keys; otherwise m
+    // already holds the exact row maxima.
     auto pass = [&](auto ROLE, bool set_m) __attribute__((always_inline)) {
         constexpr int R = decltype(ROLE)::value;
         // an opaque copy of the lane index: the per-lane LDS and global
@@ -341,126 +358,164 @@ attn_fwd_kernel(const KernelArgs a) {
         // and are not hoisted above it, where both roles' sets would be live
         const int saved[5] = {lane, l32, g, dma_r, dma_p};
         asm volatile("" : "+v"(lane), "+v"(l32), "+v"(g), "+v"(dma_r), "+v"(dma_p));
+        form_addresses();
+        if constexpr (sizeof(TIn) == 2) form_copy_offsets();
+        l = 0.f;
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-            l[rb] = 0.f;
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[rb][db][r] = 0.f;
+            for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+        // prologue copies: group 0 brings K(0), V(0), K(2); group 1 K(1), V(1)
+        if (R == 0) {
+            issue(kst(IC<0>{}), false, 0);
+            issue(vst(IC<0>{}), true, 0);
+            if (n_tiles > 2) issue(kst(IC<2>{}), false, 2);
+        } else if (n_tiles > 1) {
+            issue(kst(IC<1>{}), false, 1);
+            issue(vst(IC<1>{}), true, 1);
         }
-        if (R == 1) issue(IC<0>{}, false, 0);
-        __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
-        __syncthreads();
-        if (set_m) {
-            f32x16 sacc[2];
-            scores(sacc, kstage(IC<0>{}), 0);
-            float sv[2][16], mx[2];
-            masked_scores(0 >= first_masked_sub, sacc, sv, 0);
-            row_max(sv, mx);
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb) m[rb] = (mx[rb] == -INFINITY) ? 0.f : mx[rb];
+        wait_copies();
+        lds_barrier();
+        f32x16 snext[2];       // role 1: scores of its next tile, across the period boundary
+        uint32_t pprev[2][8];  // role 0: P of its previous tile, across the period boundary
+        if (R == 1) {
+            scores(snext, IC<0>{}, no_hook);
+            if (set_m) fix_m(snext);
         }
-        auto period = [&](auto PAR, int T) __attribute__((always_inline)) {
+        // period T (T < n_live, a tile this wave computes): role 0 runs
+        // P·V(T-1), scores(T), softmax(T); role 1 softmax(T), P·V(T),
+        // scores(T+1). Copies by group T % 2: K(T+3) and V(T+2), one LDS-DMA
+        // per four MFMAs of the period's two chains, so that the copy engine
+        // is fed at its own pace instead of stalling a wave on a burst.
+        auto copy_job = [&](auto PAR, int T, int j) __attribute__((always_inline)) {
             constexpr int P = decltype(PAR)::value;
-            const bool masked = T >= n_plain;
-            if constexpr (R == 0) {
-                if (T > 0) pv(ROLE, IC<P ^ 1>{});
-                score_softmax(ROLE, PAR, T, masked);
-            } else {
-                if (T + 1 < n_tiles) issue(IC<P ^ 1>{}, false, T + 1);
-                issue(PAR, true, T);
-                score_softmax(ROLE, PAR, T, masked);
-                if (T > 0) pv(ROLE, IC<P ^ 1>{});
-            }
-            __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's DMAs landed
-            __syncthreads();
+            // window j of K(T+3) (j < DPC), else of V(T+2); no branch on
+            // whether the tile exists (see issue_one)
+            if (j < DPC)
+                issue_one(kst(IC<(P + 3) % NS>{}), false, T + 3, j);
+            else
+                issue_one(vst(IC<(P + 2) % NS>{}), true, T + 2, j - DPC);
         };
-        for (int T = 0; T < n_tiles; T += 2) {
+        auto period = [&](auto PAR, int T) __attribute__((always_inline)) {
+            constexpr int P = decltype(PAR)::value;  // T % NS
+            constexpr bool copier = (P & 1) == R;    // T % 2 == R
+            const bool masked = T >= n_plain;
+            // P·V: jobs 0 .. DPC-1; scores: jobs DPC .. 2 DPC-1
+            auto pv_hook = [&](int f) __attribute__((always_inline)) {
+                if constexpr (copier)
+                    if ((f & 3) == 3) copy_job(PAR, T, f >> 2);
+            };
+            auto sc_hook = [&](int f) __attribute__((always_inline)) {
+                if constexpr (copier)
+                    if ((f & 3) == 3) copy_job(PAR, T, DPC + (f >> 2));
+            };
+            if constexpr (R == 0) {
+                if (P != 0 || T > 0) {
+                    pv(pprev, (P + NS - 1) % NS * C::TILE * 2, pv_hook);
+                } else if constexpr (copier) {
+#pragma unroll
+                    for (int j = 0; j < DPC; ++j) copy_job(PAR, T, j);
+                }
+                f32x16 s[2];
+                scores(s, PAR, sc_hook);
+                if (T == 0 && set_m) fix_m(s);
+                softmax(s, pprev, T, masked);
+            } else {
+                uint32_t pk[2][8];
+                softmax(snext, pk, T, masked);
+                pv(pk, P * C::TILE * 2, pv_hook);
+                // the next tile's scores; unused when that tile is not live
+                // (its stage then holds finite stale data or zeros)
+                scores(snext, IC<(P + 1) % NS>{}, sc_hook);
+            }
+            if constexpr (!copier) wait_copies();  // this group's copies of the previous period
+            lds_barrier();
+        };
+        // period T >= n_live (causal: no key of the tile is visible to this
+        // wave's rows): copy duty only, and role 0's P·V of its last tile
+        auto tail_period = [&](auto PAR, int T) __attribute__((always_inline)) {
+            constexpr int P = decltype(PAR)::value;
+            constexpr bool copier = (P & 1) == R;
+            if (R == 0 && T == n_live) pv(pprev, (P + NS - 1) % NS * C::TILE * 2, no_hook);
+            if constexpr (copier)
+#pragma unroll
+                for (int j = 0; j < 2 * DPC; ++j) copy_job(PAR, T, j);
+            if constexpr (!copier) wait_copies();
+            lds_barrier();
+        };
+        for (int T = 0; T < n_live; T += NS) {
             period(IC<0>{}, T);
-            if (T + 1 < n_tiles) period(IC<1>{}, T + 1);
+            if (T + 1 < n_live) period(IC<1>{}, T + 1);
+            if (T + 2 < n_live) period(IC<2>{}, T + 2);
+            if (T + 3 < n_live) period(IC<3>{}, T + 3);
         }
-        if ((n_tiles - 1) & 1)
-            pv(ROLE, IC<1>{});
-        else
-            pv(ROLE, IC<0>{});
+        for (int T = n_live & ~(NS - 1); T < n_tiles; T += NS) {
+            if (T >= n_live) tail_period(IC<0>{}, T);
+            if (T + 1 >= n_live && T + 1 < n_tiles) tail_period(IC<1>{}, T + 1);
+            if (T + 2 >= n_live && T + 2 < n_tiles) tail_period(IC<2>{}, T + 2);
+            if (T + 3 >= n_live && T + 3 < n_tiles) tail_period(IC<3>{}, T + 3);
+        }
+        if (R == 0 && n_live == n_tiles) pv(pprev, (n_tiles - 1) % NS * C::TILE * 2, no_hook);
+        wait_copies();  // no copy outlives the pass
         lane = saved[0], l32 = saved[1], g = saved[2], dma_r = saved[3], dma_p = saved[4];
-    };
-    // normalizer of each row = this lane's part + the other lane half + partner
-    __shared__ float l_share[C::NWAVE][2][32];
-    __shared__ int wave_bad[C::NWAVE];
-    float l_row[2];
-    auto combine_l = [&]() __attribute__((always_inline)) {
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-            l_row[rb] = xhalf_sum(l[rb]);
-            if (g == 0) l_share[w][rb][l32] = l_row[rb];
-        }
-        __syncthreads();
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) l_row[rb] += l_share[w ^ 4][rb][l32];
     };
 
     // ---- fast pass with m fixed by each row's first 32 keys; if some row's
     // normalizer leaves [0, 2^32] (every p <= 2^32 when it does not), the
     // exact row maxima are found and the pass runs again (rare) -----------
     constexpr float kMaxL = 4294967296.0f;
+    float l_row;
     for (bool exact = false;; exact = true) {
         if (role == 0)
             pass(IC<0>{}, !exact);
         else
             pass(IC<1>{}, !exact);
-        combine_l();
+        l_row = xhalf_sum(l);
         if (exact) break;
-        bool bad = false;
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) bad |= !(l_row[rb] <= kMaxL);  // also catches inf and NaN
+        const bool bad = !(l_row <= kMaxL);  // also catches inf and NaN
         if (lane == 0) wave_bad[w] = __builtin_amdgcn_ballot_w64(bad) != 0;
-        __syncthreads();
+        lds_barrier();
         bool wg_bad = false;
 #pragma unroll
         for (int i = 0; i < C::NWAVE; ++i) wg_bad |= wave_bad[i] != 0;
         if (!wg_bad) break;
-        float M[2] = {-INFINITY, -INFINITY};
+        float M = -INFINITY;
+        form_addresses();
         for (int T = 0; T < n_tiles; ++T) {
-            __syncthreads();  // the previous tile's K stage is no longer read
-            if (role == 1) issue(IC<0>{}, false, T);
-            __builtin_amdgcn_s_waitcnt(0x3f70);
-            __syncthreads();
+            lds_barrier();  // the previous tile's K stage is no longer read
+            if (role == 0) issue(kst(IC<0>{}), false, T);
+            wait_copies();
+            lds_barrier();
+            if (T < n_live) {
+                f32x16 s[2];
+                scores(s, IC<0>{}, no_hook);
+                mask(s, T);
+                float x = -INFINITY;
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                f32x16 sacc[2];
-                scores(sacc, kstage(IC<0>{}), 32 * half);
-                float sv[2][16], mx[2];
-                masked_scores(true, sacc, sv, 2 * T + half);
-                row_max(sv, mx);
-                M[0] = fmaxf(M[0], mx[0]);
-                M[1] = fmaxf(M[1], mx[1]);
+                for (int js = 0; js < 2; ++js)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) x = fmaxf(x, s[js][r]);
+                M = fmaxf(M, xhalf_max(x) * a.c);
             }
         }
-        __syncthreads();  // K stage 0 and l_share are free again
-        m[0] = (M[0] == -INFINITY) ? 0.f : M[0];
-        m[1] = (M[1] == -INFINITY) ? 0.f : M[1];
+        lds_barrier();  // K stage 0 and wave_bad are free again
+        m = (M == -INFINITY) ? 0.f : M;
     }
 
     // ---- O = Oᵀ / l (one reciprocal per row), logsumexp ---------------------
+    const float inv_l = 1.0f / l_row;
+    if (row < a.Nq) {
+        TIn *orow = Op + (int64_t)row * a.o_sn;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        const int row = prow0 + 32 * rb + l32;
-        const float inv_l = 1.0f / l_row[rb];
-        if (row < a.Nq) {
-            TIn *orow = Op + (int64_t)row * a.o_sn;
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int col = 32 * (NDB * role + db) + acc_row(4 * rr, g);
-                    store4(orow + col, oacc[rb][db][4 * rr] * inv_l, oacc[rb][db][4 * rr + 1] * inv_l,
-                           oacc[rb][db][4 * rr + 2] * inv_l, oacc[rb][db][4 * rr + 3] * inv_l);
-                }
-            if (role == 0 && g == 0 && a.lse)
-                a.lse[((int64_t)b * a.Hq + h) * a.Nq + row] = (m[rb] + log2f(l_row[rb])) * 0.69314718055994531f;
-        }
+            for (int rr = 0; rr < 4; ++rr) {
+                const int col = 32 * db + acc_row(4 * rr, g);
+                store4(orow + col, oacc[db][4 * rr] * inv_l, oacc[db][4 * rr + 1] * inv_l,
+                       oacc[db][4 * rr + 2] * inv_l, oacc[db][4 * rr + 3] * inv_l);
+            }
+        if (g == 0 && a.lse)
+            a.lse[((int64_t)b * a.Hq + h) * a.Nq + row] = (m + log2f(l_row)) * 0.69314718055994531f;
     }
 #endif
 }

@@ -157,6 +157,29 @@ __device__ __forceinline__ const __bf16 *vt_read_ptr(const __bf16 *Vs, int db, i
     return Vs + vr * D + 8 * v_chunk<D>(vr, col >> 3) + (col & 7);
 }
 
+// LDS byte address of an LDS location (the 32-bit address DS instructions take).
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(lds_void *)p;
+}
+
+// 16 bytes from LDS byte address a (one ds_read_b128).
+__device__ __forceinline__ bf16x8 lds_read_b128(uint32_t a) {
+    return *(const __attribute__((address_space(3))) bf16x8 *)(uintptr_t)a;
+}
+
+// vt_frag(Vs, db, kc, lane) from the address p = vt_read_ptr(Vs, db, lane) as
+// an LDS byte address: the key chunk only moves the address by whole rows.
+template <int D>
+__device__ __forceinline__ bf16x8 vt_frag_at(uint32_t p, int kc) {
+    i16x4 half[2];
+#pragma unroll
+    for (int hr = 0; hr < 2; ++hr)
+        half[hr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4 *)(uintptr_t)(p + (16 * kc + 8 * hr) * D * 2));
+    const i16x8 v8 = __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v8);
+}
+
 // LDS-DMA: 16 bytes from gptr (per lane) into LDS at lds_base + 16 * lane,
 // lds_base wave-uniform (it goes through M0). Issued as inline assembly so
 // that the compiler does not treat it as a store that every later LDS read
