@@ -105,6 +105,9 @@ attn_fwd_kernel(const KernelArgs a) {
     using C = TileCfg<D>;
     constexpr int TQ = C::TQ, TK = C::TK, CPR = C::CPR, NKC = C::NKC, NDB = C::NDB;
     constexpr int NS = C::NSTAGE, DPC = C::DMA_PER_COPIER;
+    // LDS fragment reads run PF MFMAs ahead of their use: enough that one
+    // wave's chain is not held up by the LDS latency
+    constexpr int PF = 4;
     __shared__ __attribute__((aligned(1024))) unsigned char lds_raw[C::LDS_BYTES];
     __shared__ int wave_bad[C::NWAVE];
     __bf16 *const Kst = (__bf16 *)lds_raw;   // K ring
@@ -274,27 +277,32 @@ attn_fwd_kernel(const KernelArgs a) {
         auto kread = [&](int f) __attribute__((always_inline)) {
             return lds_read_b128(kaddr[f >> 1] + so + (f & 1) * 32 * D * 2);
         };
-        kf[0] = kread(0);
-        kf[1] = kread(1);
+#pragma unroll
+        for (int f = 0; f < PF; ++f) kf[f] = kread(f);
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
-            if (f + 2 < NF) kf[f + 2] = kread(f + 2);
+            if (f + PF < NF) kf[f + PF] = kread(f + PF);
             s[f & 1] = mfma_32x32x16(kf[f], qf[f >> 1], s[f & 1]);
-            // a scheduling boundary: keeps the fragment reads two steps ahead
-            // rather than all hoisted (registers are the limit in this kernel)
+            // a scheduling boundary: keeps the fragment reads PF steps ahead
+            // rather than all hoisted
             asm volatile("" ::);
             hook(f);
         }
     };
-    // the causal / key-range mask on the scores of tile T
+    // the causal / key-range mask on the scores of tile T: key j of this
+    // lane's row is visible iff j < lim = min(row + 1, Nkv) (Nkv without
+    // the causal mask). With j = 64T + 32js + acc_row(r, g) and acc_row(r, g)
+    // = acc_row(r, 0) + 4g, one threshold per half and one compare against a
+    // constant per element.
     auto mask = [&](f32x16 (&s)[2], int T) __attribute__((always_inline)) {
+        const int lim = CAUSAL ? min(row + 1, a.Nkv) : a.Nkv;
 #pragma unroll
-        for (int js = 0; js < 2; ++js)
+        for (int js = 0; js < 2; ++js) {
+            const int t = lim - (TK * T + 32 * js + 4 * g);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = TK * T + 32 * js + acc_row(r, g);
-                if ((CAUSAL && key > row) || key >= a.Nkv) s[js][r] = -INFINITY;
-            }
+            for (int r = 0; r < 16; ++r)
+                if (acc_row(r, 0) >= t) s[js][r] = -INFINITY;
+        }
     };
     // m from the row's first 32 keys (tile 0, masked)
     auto fix_m = [&](f32x16 (&s)[2]) __attribute__((always_inline)) {
@@ -334,11 +342,11 @@ attn_fwd_kernel(const KernelArgs a) {
         auto vread = [&](int f) __attribute__((always_inline)) {
             return vt_frag_at<D>(vaddr[f % NDB] + so, f / NDB);
         };
-        vf[0] = vread(0);
-        vf[1] = vread(1);
+#pragma unroll
+        for (int f = 0; f < PF; ++f) vf[f] = vread(f);
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
-            if (f + 2 < NF) vf[f + 2] = vread(f + 2);
+            if (f + PF < NF) vf[f + PF] = vread(f + PF);
             const int kch = f / NDB;
             const u32x4 p = {pk[kch >> 1][4 * (kch & 1)], pk[kch >> 1][4 * (kch & 1) + 1],
                              pk[kch >> 1][4 * (kch & 1) + 2], pk[kch >> 1][4 * (kch & 1) + 3]};
@@ -420,6 +428,14 @@ attn_fwd_kernel(const KernelArgs a) {
                 scores(s, PAR, sc_hook);
                 if (T == 0 && set_m) fix_m(s);
                 softmax(s, pprev, T, masked);
+                // P and l complete before the barrier: the softmax overlaps
+                // role 1's MFMAs of this period, not the next period's start
+#pragma unroll
+                for (int js = 0; js < 2; ++js)
+                    asm volatile("" : "+v"(pprev[js][0]), "+v"(pprev[js][1]), "+v"(pprev[js][2]),
+                                 "+v"(pprev[js][3]), "+v"(pprev[js][4]), "+v"(pprev[js][5]),
+                                 "+v"(pprev[js][6]), "+v"(pprev[js][7]));
+                asm volatile("" : "+v"(l));
             } else {
                 uint32_t pk[2][8];
                 softmax(snext, pk, T, masked);
