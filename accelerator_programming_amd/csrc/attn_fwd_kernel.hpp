@@ -205,22 +205,40 @@ attn_fwd_kernel(const KernelArgs a) {
         }
     };
     // window u (0 .. DPC-1) of this wave's share of one tile
+    // LDS byte address of the K and V rings (uniform)
+    const uint32_t lds_k0 = __builtin_amdgcn_readfirstlane(lds_addr(Kst));
+    const uint32_t lds_v0 = __builtin_amdgcn_readfirstlane(lds_addr(Vst));
+    const int last_tile = (a.Nkv - 1) / TK;
+    // Buffer resource over the rows of K or V tile `tile` that exist: a load
+    // at a byte offset past the last existing row returns zeros. A tile past
+    // the last one is replaced by the last tile (its copy lands in a stage
+    // nobody reads before it is refilled). Scalar arithmetic only.
+    auto tile_rsrc = [&](bool is_v, int tile) __attribute__((always_inline)) {
+        const int32_t sn = is_v ? a.v_sn : a.k_sn;
+        const int t = min(tile, last_tile);
+        const uint32_t rows = (uint32_t)min(a.Nkv - t * TK, TK);
+        const uint64_t gb = (uint64_t)(uintptr_t)(is_v ? Vp : Kp) +
+                            (uint64_t)(uint32_t)t * ((uint64_t)(uint32_t)sn * (TK * 2));
+        return u32x4{(uint32_t)gb, (uint32_t)(gb >> 32), rows * (uint32_t)sn * 2u, 0x00020000u};
+    };
+    // window u of this wave's share of a tile into the stage at LDS byte
+    // offset stage_off of the K or V ring
+    auto dma_one = [&](const u32x4 rsrc, bool is_v, uint32_t stage_off, int u) __attribute__((always_inline)) {
+        // formed right here from one live register, not kept per copy
+        uint32_t m0 = lds_k0 + (uint32_t)cw * 1024u;
+        asm volatile("" : "+s"(m0));
+        m0 += (is_v ? NS * C::TILE * 2 : 0) + stage_off + (uint32_t)(4 * u) * 1024u;
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                     :
+                     : "s"(m0), "v"(is_v ? voff_v[u] : voff_k[u]), "s"(rsrc)
+                     : "memory");
+    };
     auto issue_one = [&](__bf16 *dst, bool is_v, int tile, int u) __attribute__((always_inline)) {
         const TIn *base = is_v ? Vp : Kp;
         const int32_t sn = is_v ? a.v_sn : a.k_sn;
         if constexpr (sizeof(TIn) == 2) {
-            // the resource covers the rows of this tile that exist; a row
-            // past the last key starts at or beyond its end (the row stride
-            // is at least D; should the offset wrap, it names an existing
-            // row, whose values are finite and masked). A tile past the last
-            // one gets an empty resource: its copy writes zeros to the
-            // (free) stage and reads nothing.
-            const int rows = max(0, min(a.Nkv - tile * TK, TK));
-            // wave-uniform; kept in an SGPR for the resource
-            const uint32_t bytes = __builtin_amdgcn_readfirstlane(
-                rows > 0 ? ((uint32_t)(rows - 1) * (uint32_t)sn + D) * 2u : 0u);
-            const u32x4 rsrc = buffer_rsrc(base + (int64_t)tile * TK * sn, bytes);
-            dma16_buf_to_lds(rsrc, is_v ? voff_v[u] : voff_k[u], dst + (4 * u + cw) * 64 * 8);
+            dma_one(tile_rsrc(is_v, tile), is_v,
+                    (uint32_t)((char *)dst - (char *)(is_v ? Vst : Kst)), u);
         } else {
             // fp32 inputs: rounded to bf16 in registers, same LDS placement
             {
@@ -395,34 +413,43 @@ attn_fwd_kernel(const KernelArgs a) {
         // scores(T+1). Copies by group T % 2: K(T+3) and V(T+2), one LDS-DMA
         // per four MFMAs of the period's two chains, so that the copy engine
         // is fed at its own pace instead of stalling a wave on a burst.
-        auto copy_job = [&](auto PAR, int T, int j) __attribute__((always_inline)) {
+        auto copy_job = [&](auto PAR, int T, int j, const u32x4 &rk, const u32x4 &rv) __attribute__((always_inline)) {
             constexpr int P = decltype(PAR)::value;
             // window j of K(T+3) (j < DPC), else of V(T+2); no branch on
-            // whether the tile exists (see issue_one)
-            if (j < DPC)
-                issue_one(kst(IC<(P + 3) % NS>{}), false, T + 3, j);
-            else
-                issue_one(vst(IC<(P + 2) % NS>{}), true, T + 2, j - DPC);
+            // whether the tile exists (see tile_rsrc)
+            if constexpr (sizeof(TIn) == 2) {
+                if (j < DPC)
+                    dma_one(rk, false, (P + 3) % NS * C::TILE * 2, j);
+                else
+                    dma_one(rv, true, (P + 2) % NS * C::TILE * 2, j - DPC);
+            } else {
+                if (j < DPC)
+                    issue_one(kst(IC<(P + 3) % NS>{}), false, T + 3, j);
+                else
+                    issue_one(vst(IC<(P + 2) % NS>{}), true, T + 2, j - DPC);
+            }
         };
         auto period = [&](auto PAR, int T) __attribute__((always_inline)) {
             constexpr int P = decltype(PAR)::value;  // T % NS
             constexpr bool copier = (P & 1) == R;    // T % 2 == R
             const bool masked = T >= n_plain;
+            u32x4 rk = {0, 0, 0, 0}, rv = {0, 0, 0, 0};
+            if constexpr (copier && sizeof(TIn) == 2) rk = tile_rsrc(false, T + 3), rv = tile_rsrc(true, T + 2);
             // P·V: jobs 0 .. DPC-1; scores: jobs DPC .. 2 DPC-1
             auto pv_hook = [&](int f) __attribute__((always_inline)) {
                 if constexpr (copier)
-                    if ((f & 3) == 3) copy_job(PAR, T, f >> 2);
+                    if ((f & 3) == 3) copy_job(PAR, T, f >> 2, rk, rv);
             };
             auto sc_hook = [&](int f) __attribute__((always_inline)) {
                 if constexpr (copier)
-                    if ((f & 3) == 3) copy_job(PAR, T, DPC + (f >> 2));
+                    if ((f & 3) == 3) copy_job(PAR, T, DPC + (f >> 2), rk, rv);
             };
             if constexpr (R == 0) {
                 if (P != 0 || T > 0) {
                     pv(pprev, (P + NS - 1) % NS * C::TILE * 2, pv_hook);
                 } else if constexpr (copier) {
 #pragma unroll
-                    for (int j = 0; j < DPC; ++j) copy_job(PAR, T, j);
+                    for (int j = 0; j < DPC; ++j) copy_job(PAR, T, j, rk, rv);
                 }
                 f32x16 s[2];
                 scores(s, PAR, sc_hook);
@@ -453,9 +480,12 @@ attn_fwd_kernel(const KernelArgs a) {
             constexpr int P = decltype(PAR)::value;
             constexpr bool copier = (P & 1) == R;
             if (R == 0 && T == n_live) pv(pprev, (P + NS - 1) % NS * C::TILE * 2, no_hook);
-            if constexpr (copier)
+            if constexpr (copier) {
+                u32x4 rk = {0, 0, 0, 0}, rv = {0, 0, 0, 0};
+                if constexpr (sizeof(TIn) == 2) rk = tile_rsrc(false, T + 3), rv = tile_rsrc(true, T + 2);
 #pragma unroll
-                for (int j = 0; j < 2 * DPC; ++j) copy_job(PAR, T, j);
+                for (int j = 0; j < 2 * DPC; ++j) copy_job(PAR, T, j, rk, rv);
+            }
             if constexpr (!copier) wait_copies();
             lds_barrier();
         };
