@@ -73,6 +73,8 @@ def lib() -> ctypes.CDLL:
                                          ctypes.POINTER(ctypes.c_int32),
                                          ctypes.POINTER(ctypes.c_int32),
                                          ctypes.POINTER(ctypes.c_int32)]
+        L.tile_gemm_bf16_nt.restype = ctypes.c_int
+        L.tile_gemm_bf16_nt.argtypes = [I64, I64, I64, P, I64, P, I64, P, I64, P]
         _lib = L
     return _lib
 

@@ -24,7 +24,7 @@ HIPCC_FLAGS = [
 ]
 
 TARGETS = {
-    "libattn_fwd.so": ["attn_fwd.hip"],
+    "libattn_fwd.so": ["attn_fwd.hip", "tile_gemm.hip"],
     "libattn_tile_selftest.so": ["tile_selftest.hip"],
 }
 

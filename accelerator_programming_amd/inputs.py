@@ -117,3 +117,36 @@ def sample_rows(w: Workload, n: int, seed: int = 7) -> torch.Tensor:
     rnd = torch.stack([b, h, i], dim=1)
     rows = torch.cat([torch.tensor(fixed, dtype=torch.int64), rnd], dim=0)[:n]
     return rows
+
+
+@dataclass(frozen=True)
+class GemmWorkload:
+    """C = A·Bᵀ with A [M, K] and B [N, K] bf16, drawn i.i.d. N(0, 1)."""
+    name: str
+    M: int
+    N: int
+    K: int
+    seed: int
+
+    def flops(self) -> float:
+        return 2.0 * self.M * self.N * self.K
+
+    def io_bytes(self) -> int:
+        return 2 * (self.M * self.K + self.N * self.K + self.M * self.N)
+
+
+# The projections on either side of the Llama-3.1-8B-shaped attention (C3:
+# batch 2 x 4096 tokens, d_model 4096, 32 query and 8 kv heads of 128): the
+# fused Q/K/V projection (N = (32 + 8 + 8) * 128) and the O projection.
+G1 = GemmWorkload("G1_M8192_N6144_K4096_qkv_proj", 8192, 6144, 4096, 3001)
+G2 = GemmWorkload("G2_M8192_N4096_K4096_o_proj", 8192, 4096, 4096, 3002)
+GEMM_WORKLOADS = {w.name.split("_")[0]: w for w in (G1, G2)}
+
+
+def make_gemm_inputs(w: GemmWorkload, device: str | torch.device = "cpu"):
+    """Return (a, b): A [M, K] then B [N, K], fp32 N(0, 1) draws rounded to bf16."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed)
+    a = torch.randn((w.M, w.K), generator=g, dtype=torch.float32)
+    b = torch.randn((w.N, w.K), generator=g, dtype=torch.float32)
+    return a.to(torch.bfloat16).to(device), b.to(torch.bfloat16).to(device)
