@@ -194,34 +194,48 @@ gemm_bf16_nt_kernel(const GemmArgs a) {
     wait_copies();
     barrier();
 
-    // ---- K loop, two steps per iteration so that whether this wave copies
-    // in a step is known at compile time (COPIER). Past the last step the
-    // copy re-reads the last step's slabs into a stage no later step reads.
+    // ---- K loop. The fragments of a k-substep are read one substep ahead
+    // (two register sets), and those of the next step's first substep at the
+    // end of this step: that stage was published by the barrier of the step
+    // before, so only the copy ring needs the barrier that closes a step.
+    // Two steps per iteration, so that whether this wave copies in a step is
+    // known at compile time (COPIER). Past the last step the copy re-reads
+    // the last step's slabs (the same bytes) into that step's stage.
+    bf16x8 xa[2][4], xb[2][4];
+    auto load = [&](int set, uint32_t so, int kk) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            xb[set][i] = lds_read_b128(fb[i][kk] + so);
+            xa[set][i] = lds_read_b128(fa[i][kk] + so);
+        }
+    };
+    auto mma = [&](int set, int tc, int kk, auto COPIER) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                acc[i][j] = mfma_32x32x16(xb[set][i], xa[set][j], acc[i][j]);
+                if constexpr (decltype(COPIER)::value)
+                    if ((j & 1) == 1) copy_one(tc, 8 * kk + 2 * i + (j >> 1));
+            }
+    };
     auto step = [&](int t, auto COPIER) __attribute__((always_inline)) {
         const uint32_t so = (uint32_t)(t % NS) * C::STAGE_BYTES;
+        const uint32_t so_next = (uint32_t)((t + 1) % NS) * C::STAGE_BYTES;
         const int tc = min(t + 3, n_steps - 1);
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            bf16x8 xa[4], xb[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                xb[i] = lds_read_b128(fb[i][kk] + so);
-                xa[i] = lds_read_b128(fa[i][kk] + so);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    acc[i][j] = mfma_32x32x16(xb[i], xa[j], acc[i][j]);
-                    if constexpr (decltype(COPIER)::value)
-                        if ((j & 1) == 1) copy_one(tc, 8 * kk + 2 * i + (j >> 1));
-                }
-        }
+        load(1, so, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(0, tc, 0, COPIER);
+        __builtin_amdgcn_sched_barrier(0);
+        load(0, so_next, 0);  // unused after the last step (a finite stage)
+        __builtin_amdgcn_sched_barrier(0);
+        mma(1, tc, 1, COPIER);
         if constexpr (!decltype(COPIER)::value) wait_copies();  // this group's copies of step t-1
         barrier();
     };
     auto k_loop = [&](auto G) __attribute__((always_inline)) {
         constexpr int GR = decltype(G)::value;
+        load(0, 0, 0);
         for (int t = 0; t < n_steps; t += 2) {
             step(t, std::integral_constant<bool, GR == 0>{});
             if (t + 1 < n_steps) step(t + 1, std::integral_constant<bool, GR == 1>{});

@@ -41,6 +41,15 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
+def gemm_source_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "accelerator_programming_amd", "csrc")
+    for name in ("gemm_kernel.hpp", "tile_gemm.hip", "tile.hpp"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
 def kernel_name(w):
     """The kernel the library launches for workload w (as rocprofv3 names it)."""
     causal = "true" if w.causal else "false"
@@ -53,7 +62,7 @@ def kernel_name(w):
         w.dqk, causal, "__bf16" if str(w.dtype) == "torch.bfloat16" else "float")
 
 
-def traffic_for_current_kernel(workload_name: str, tag: str):
+def traffic_for_current_kernel(workload_name: str, tag: str, sha=None):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None when it was taken on other kernel sources or another workload."""
     try:
@@ -61,7 +70,7 @@ def traffic_for_current_kernel(workload_name: str, tag: str):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_sha") != kernel_source_sha() or t.get("workload") != workload_name:
+    if t.get("kernel_sha") != (sha or kernel_source_sha()) or t.get("workload") != workload_name:
         return None
     return t.get("bytes_per_launch")
 
@@ -103,12 +112,109 @@ def cpu_baseline(w, q, k, v, target_s: float, threads: int):
     }
 
 
+def gemm_cpu_baseline(w, a, b, target_s: float, threads: int):
+    """Time the fp64 GEMM oracle on a sample of C rows sized for about target_s."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle.gemm import gemm_fp64
+
+    A = a.float().cpu().numpy()
+    B = b.float().cpu().numpy()
+    rng = np.random.default_rng(123)
+
+    def timed(n):
+        rows = rng.integers(0, w.M, n)
+        with threadpool_limits(limits=threads):
+            t0 = time.perf_counter()
+            gemm_fp64(A, B, rows=rows)
+            return time.perf_counter() - t0, 2.0 * n * w.N * w.K, n
+
+    dt, fl, n = timed(64)
+    n2 = int(min(max(n * target_s / max(dt, 1e-3), n), w.M))
+    dt, fl, n = timed(n2)
+    return {
+        "value": fl / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "%d seeded rows of C of %s (fp64 product through numpy's BLAS, %d threads); "
+                  "%.1f s wall, %.3g FLOP" % (n, w.name, threads, dt, fl),
+    }
+
+
+def gemm_main(args, w) -> int:
+    """One step = one C = A·Bᵀ launch over the workload's full shape."""
+    import torch
+
+    from accelerator_programming_amd import gemm
+    from accelerator_programming_amd.inputs import make_gemm_inputs
+
+    torch.cuda.set_device(0)
+    a, b = make_gemm_inputs(w, "cuda")
+    c = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        gemm.gemm_nt(a, b, out=c, stream=stream)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        gemm.gemm_nt(a, b, out=c, stream=stream)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_avg_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    flops = w.flops()
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (kern_avg_ms * 1e-3) / 1e12
+    finite = bool(torch.isfinite(c).all().item())
+    cpu = None
+    if not args.no_cpu_baseline:
+        threads = min(16, len(os.sched_getaffinity(0)))
+        cpu = gemm_cpu_baseline(w, a, b, args.cpu_seconds, threads)
+    line = {
+        "metric": "bf16 GEMM C = A·Bᵀ TFLOP/s on 1 MI355X",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) inputs, resident in HBM)",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K,
+                   "gflop_per_step": round(flops / 1e9, 3), "parallelism": "single-gpu",
+                   "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+                   "outputs_finite": finite},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_for_current_kernel(w.name, "tile_gemm_" + args.config,
+                                                           gemm_source_sha()),
+                     "kernel_ms_avg": round(kern_avg_ms, 4),
+                     "kernel": "attn::gemm_bf16_nt_kernel"},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0 if finite else 1
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="C4", help="workload C1..C5 (the metric is quoted on C4)")
+    ap.add_argument("--config", default="C4",
+                    help="workload C1..C5 (the metric is quoted on C4), D1/D2 (split-KV decode) "
+                         "or G1/G2 (the bf16 GEMM of the projections)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -135,8 +241,10 @@ def main() -> int:
         return 0
 
     from accelerator_programming_amd import attn
-    from accelerator_programming_amd.inputs import WORKLOADS, make_inputs
+    from accelerator_programming_amd.inputs import GEMM_WORKLOADS, WORKLOADS, make_inputs
 
+    if args.config in GEMM_WORKLOADS:
+        return gemm_main(args, GEMM_WORKLOADS[args.config])
     w = WORKLOADS[args.config]
     torch.cuda.set_device(0)
     q, k, v = make_inputs(w, "cuda")
