@@ -1,7 +1,7 @@
 """ctypes binding of the C ABI in include/attn_fwd.h (argument marshalling only).
 
 The names mirror the C entry points: ``attn_fwd_create``,
-``attn_fwd_create_ex``, ``attn_fwd_run``, ``attn_fwd_destroy``,
+``attn_fwd_create_ex``, ``attn_fwd_run``, ``attn_fwd_run_dropout``, ``attn_fwd_destroy``,
 ``attn_status_str`` and ``attn_fwd_plan_info``. Every step of the attention
 pass runs inside the HIP library; torch only provides device memory and the
 stream. If the library has not been built this module raises on first use:
@@ -73,6 +73,8 @@ def lib() -> ctypes.CDLL:
                                          ctypes.POINTER(ctypes.c_int32),
                                          ctypes.POINTER(ctypes.c_int32),
                                          ctypes.POINTER(ctypes.c_int32)]
+        L.attn_fwd_run_dropout.restype = ctypes.c_int
+        L.attn_fwd_run_dropout.argtypes = [P, P, P, P, P, P, ctypes.c_float, ctypes.c_uint64, P]
         L.tile_gemm_bf16_nt.restype = ctypes.c_int
         L.tile_gemm_bf16_nt.argtypes = [I64, I64, I64, P, I64, P, I64, P, I64, P]
         _lib = L
@@ -206,6 +208,23 @@ class AttnFwd:
                      lse.data_ptr() if lse is not None else None, s.cuda_stream)
 
     __call__ = run
+
+    def run_dropout(self, q, k, v, o, lse=None, p_drop: float = 0.0, seed: int = 0,
+                    stream=None) -> None:
+        """attn_fwd_run_dropout: dropout at probability floor(256 p_drop) / 256
+        with the counter-based generator keyed by ``seed``."""
+        import torch
+        for t in (q, k, v, o) + ((lse,) if lse is not None else ()):
+            if not t.is_cuda:
+                raise ValueError("attn_fwd_run_dropout needs device tensors")
+        if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
+            raise ValueError("lse must be a contiguous float32 tensor")
+        s = stream if stream is not None else torch.cuda.current_stream()
+        st = lib().attn_fwd_run_dropout(self.plan, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                        o.data_ptr(), lse.data_ptr() if lse is not None else None,
+                                        float(p_drop), int(seed) & (2 ** 64 - 1), s.cuda_stream)
+        if st != ATTN_OK:
+            raise AttnError(st, "attn_fwd_run_dropout")
 
     def split_count(self) -> int:
         return attn_fwd_split_count(self.plan)

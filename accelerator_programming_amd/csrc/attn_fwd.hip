@@ -109,9 +109,9 @@ attn_status validate(const attn_fwd_params *in, attn_fwd_plan *out) {
     return ATTN_OK;
 }
 
-template <int D, bool CAUSAL, typename T>
+template <int D, bool CAUSAL, typename T, bool DROP = false>
 hipError_t launch(const attn_fwd_plan *pl, const KernelArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL((attn::attn_fwd_kernel<D, CAUSAL, T>), dim3((uint32_t)pl->grid),
+    hipLaunchKernelGGL((attn::attn_fwd_kernel<D, CAUSAL, T, DROP>), dim3((uint32_t)pl->grid),
                        dim3(pl->block), 0, stream, a);
     return hipGetLastError();
 }
@@ -165,6 +165,9 @@ KernelArgs make_args(const attn_fwd_plan *plan, const void *Q, const void *K, co
     a.c = plan->c;
     a.v_in_k = (V == K && p.v_strides[0] == p.k_strides[0] && p.v_strides[1] == p.k_strides[1] &&
                 p.v_strides[2] == p.k_strides[2]) ? 1 : 0;
+    a.drop_thr = 0;
+    a.seed_lo = a.seed_hi = 0;
+    a.drop_scale = 1.0f;
     return a;
 }
 
@@ -272,6 +275,45 @@ attn_status attn_fwd_run(const attn_fwd_plan *plan, const void *Q, const void *K
             break;
         case V_D576_BF16:
             e = p.causal ? launch_wide<true>(plan, a, s) : launch_wide<false>(plan, a, s);
+            break;
+        default:
+            return ATTN_ERR_INVALID;
+    }
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_fwd_run_dropout(const attn_fwd_plan *plan, const void *Q, const void *K,
+                                 const void *V, void *O, float *lse, float p_drop, uint64_t seed,
+                                 void *stream) {
+    if (!plan || !Q || !K || !V || !O) return ATTN_ERR_INVALID;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) ||
+        (lse && ((uintptr_t)lse & 3u)))
+        return ATTN_ERR_INVALID;
+    if (!(p_drop >= 0.0f && p_drop < 1.0f)) return ATTN_ERR_INVALID;  // also NaN
+    if (plan->variant == V_D576_BF16) return ATTN_ERR_UNSUPPORTED;
+    // the drop probability is taken in steps of 1/256
+    const uint32_t thr = (uint32_t)((double)p_drop * 256.0);
+    if (thr == 0) return attn_fwd_run(plan, Q, K, V, O, lse, stream);
+    const attn_fwd_params &p = plan->p;
+    KernelArgs a = make_args(plan, Q, K, V, O, lse);
+    a.drop_thr = thr;
+    a.seed_lo = (uint32_t)seed;
+    a.seed_hi = (uint32_t)(seed >> 32);
+    a.drop_scale = (float)(256.0 / (256.0 - (double)thr));
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    switch (plan->variant) {
+        case V_D64_BF16:
+            e = p.causal ? launch<64, true, __bf16, true>(plan, a, s)
+                         : launch<64, false, __bf16, true>(plan, a, s);
+            break;
+        case V_D128_BF16:
+            e = p.causal ? launch<128, true, __bf16, true>(plan, a, s)
+                         : launch<128, false, __bf16, true>(plan, a, s);
+            break;
+        case V_D64_FP32:
+            e = p.causal ? launch<64, true, float, true>(plan, a, s)
+                         : launch<64, false, float, true>(plan, a, s);
             break;
         default:
             return ATTN_ERR_INVALID;

@@ -71,7 +71,35 @@ struct KernelArgs {
     int32_t n_qtiles;
     float c;         // softmax scale * log2(e)
     int32_t v_in_k;  // V is the first d_v columns of K's rows (same pointer and strides)
+    // dropout (kernels instantiated with DROP only): drop probability
+    // drop_thr / 256, generator key (seed_lo, seed_hi), drop_scale =
+    // 256 / (256 - drop_thr)
+    uint32_t drop_thr, seed_lo, seed_hi;
+    float drop_scale;
 };
+
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC'11): ten rounds of two 32x32 -> 64-bit products whose
+// high halves are xored with the other two words and the key, the key
+// advanced by the Weyl constants between rounds. Counter-based: the output
+// depends only on (ctr, key), so any element's random bits can be produced
+// where that element is.
+__device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint32_t hi0 = __umulhi(0xD2511F53u, c[0]), lo0 = 0xD2511F53u * c[0];
+        const uint32_t hi1 = __umulhi(0xCD9E8D57u, c[2]), lo1 = 0xCD9E8D57u * c[2];
+        const uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+        c[0] = n0;
+        c[1] = lo1;
+        c[2] = n2;
+        c[3] = lo0;
+    }
+}
 
 template <int D>
 struct TileCfg {
@@ -98,7 +126,7 @@ struct TileCfg {
 template <int N>
 using IC = std::integral_constant<int, N>;
 
-template <int D, bool CAUSAL, typename TIn>
+template <int D, bool CAUSAL, typename TIn, bool DROP = false>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_kernel(const KernelArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
@@ -331,6 +359,29 @@ attn_fwd_kernel(const KernelArgs a) {
         x = xhalf_max(x) * a.c;
         m = (x == -INFINITY) ? 0.f : x;
     };
+    // Dropout of the rounded P of tile T, after its row sum (the normalizer is
+    // that of the softmax before dropout): element (row, key j) is kept when
+    // its byte of Philox4x32-10 is >= drop_thr, with key (seed_lo, seed_hi),
+    // counter (row, 2 (j / 32) + (j / 4) mod 2, b H_q + h, 0) and the byte
+    // t = j mod 4 of output word (j / 8) mod 4. A lane's 16 keys of one
+    // 32-key half are 8q + 4g + t (q, t < 4): one counter, all 16 bytes.
+    // The kept values are scaled by 256 / (256 - drop_thr) at the end.
+    auto drop = [&](uint32_t (&pk)[2][8], int T) __attribute__((always_inline)) {
+#pragma unroll
+        for (int js = 0; js < 2; ++js) {
+            uint32_t w[4] = {(uint32_t)row, (uint32_t)(2 * (2 * T + js) + g),
+                             (uint32_t)(b * a.Hq + h), 0u};
+            philox4x32_10(w, a.seed_lo, a.seed_hi);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                // elements 2j, 2j + 1: word j / 2, bytes 2 (j % 2) and 2 (j % 2) + 1
+                const uint32_t x = w[j >> 1] >> (16 * (j & 1));
+                const uint32_t lo = ((x & 0xFFu) >= a.drop_thr) ? 0x0000FFFFu : 0u;
+                const uint32_t hi = (((x >> 8) & 0xFFu) >= a.drop_thr) ? 0xFFFF0000u : 0u;
+                pk[js][j] &= lo | hi;
+            }
+        }
+    };
     // p = 2^(s·c - m) (Map(exp)) rounded to bf16 into pk, and the partial row
     // sum of the rounded p (what P·V multiplies; Reduce(+)), two at a time
     // with v_dot2_f32_bf16 in independent partial sums
@@ -350,6 +401,7 @@ attn_fwd_kernel(const KernelArgs a) {
             for (int j = 0; j < 8; ++j) ls[j & 3] = sum_bf16x2(pk[js][j], ls[j & 3]);
         }
         l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+        if constexpr (DROP) drop(pk, T);
     };
     // Oᵀ += Vᵀ·Pᵀ over one tile (V stage at byte offset so); the 16-key chunk
     // kch of Pᵀ is pk[kch / 2][4 (kch % 2) .. + 3]
@@ -549,7 +601,7 @@ attn_fwd_kernel(const KernelArgs a) {
     }
 
     // ---- O = Oᵀ / l (one reciprocal per row), logsumexp ---------------------
-    const float inv_l = 1.0f / l_row;
+    const float inv_l = DROP ? a.drop_scale / l_row : 1.0f / l_row;
     if (row < a.Nq) {
         TIn *orow = Op + (int64_t)row * a.o_sn;
 #pragma unroll

@@ -103,6 +103,27 @@ attn_status attn_fwd_run(const attn_fwd_plan *plan, const void *Q, const void *K
                          const void *V, void *O, float *lse, void *stream);
 
 /*
+ * attn_fwd_run_dropout - attn_fwd_run with dropout between the softmax and
+ * the product with V ("CS149 L11: Programming Specialized Hardware", section
+ * 5, slide 54: Q·Kᵀ, Mask, Softmax, Dropout, ×V). Every probability p_ij is
+ * replaced by p_ij * keep_ij / (1 - q) with q = floor(256 * p_drop) / 256
+ * (the drop probability is taken in steps of 1/256); logsumexp stays that of
+ * the softmax before dropout. keep_ij = [byte_ij >= 256 q], where byte_ij is
+ * one byte of the counter-based generator Philox4x32-10 (Salmon et al.,
+ * SC'11) with key (seed mod 2^32, seed / 2^32), counter
+ * (i, 2 (j / 32) + (j / 4) mod 2, b H_q + h, 0), output word (j / 8) mod 4,
+ * byte j mod 4 - so the mask depends only on (seed, b, h, i, j) and is the
+ * same for any launch configuration.
+ * p_drop must be in [0, 1) (ATTN_ERR_INVALID otherwise, also for NaN);
+ * q == 0 runs attn_fwd_run. Served for d = 64 and d = 128 (bf16, and fp32 at
+ * d = 64); the wide-head variant returns ATTN_ERR_UNSUPPORTED. Pointers,
+ * alignment and stream as for attn_fwd_run.
+ */
+attn_status attn_fwd_run_dropout(const attn_fwd_plan *plan, const void *Q, const void *K,
+                                 const void *V, void *O, float *lse, float p_drop,
+                                 uint64_t seed, void *stream);
+
+/*
  * Split-KV forward (few query rows per kv head, long key sequences: decode).
  * The keys of each kv head are cut into n_splits contiguous ranges; each
  * range's attention of all the group's query rows is computed separately and

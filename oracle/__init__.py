@@ -6,8 +6,8 @@ import this package. It computes the plain definition of attention forward
 "CS149 L11: Programming Specialized Hardware", section 5, slides 48 and 54)
 in fp64 C code (``attn_oracle.c``), and shares nothing with the HIP library.
 
-Function:
-    attention_fp64(q, k, v, causal, scale, rows=None, threads=0)
+Functions:
+    attention_fp64(q, k, v, causal, scale, rows=None, threads=0, drop_thr=0, seed=0)
         q: [B, H_q, N_q, d_qk], k: [B, H_kv, N_kv, d_qk], v: [B, H_kv, N_kv, d_v]
         (torch tensors or numpy arrays of any float dtype; values are widened
         to fp32, which is exact for bf16 and fp32 inputs).
@@ -16,6 +16,11 @@ Function:
         O is [R, d_v] and lse is [R]. Without rows, O is [B, H_q, N_q, d_v]
         and lse is [B, H_q, N_q].
         Returns (O, lse, threads_used) as float64 numpy arrays and an int.
+        drop_thr (1..255) applies dropout at probability drop_thr / 256: each
+        p_j is kept (and scaled by 256 / (256 - drop_thr)) when its byte of
+        the counter-based generator Philox4x32-10 is >= drop_thr; lse is that
+        of the softmax before dropout.
+    philox4x32_10(ctr, key): one block of that generator.
 """
 from __future__ import annotations
 
@@ -49,6 +54,13 @@ def _bind_lib(path: str):
     I = ctypes.c_int64
     f.argtypes = [P, P, P, I, I, I, I, I, I, I, ctypes.c_int, ctypes.c_float,
                   P, I, P, P, ctypes.c_int]
+    f = lib.attn_oracle_dropout_fp64
+    f.restype = ctypes.c_int
+    f.argtypes = [P, P, P, I, I, I, I, I, I, I, ctypes.c_int, ctypes.c_float,
+                  P, I, P, P, ctypes.c_int, ctypes.c_uint32, ctypes.c_uint64]
+    f = lib.oracle_philox4x32_10
+    f.restype = None
+    f.argtypes = [P, P, P]
     return lib
 
 
@@ -71,10 +83,22 @@ def _as_f32(x) -> np.ndarray:
     return np.ascontiguousarray(np.asarray(x, dtype=np.float32))
 
 
+def philox4x32_10(ctr, key) -> np.ndarray:
+    """The oracle's Philox4x32-10 block: 4 uint32 counter words, 2 key words
+    -> 4 uint32 output words."""
+    c = np.ascontiguousarray(np.asarray(ctr, dtype=np.uint32).reshape(4))
+    k = np.ascontiguousarray(np.asarray(key, dtype=np.uint32).reshape(2))
+    out = np.empty(4, dtype=np.uint32)
+    _load().oracle_philox4x32_10(c.ctypes.data, k.ctypes.data, out.ctypes.data)
+    return out
+
+
 def attention_fp64(q, k, v, causal: bool, scale: float, rows=None, threads: int = 0,
-                   lib_path: str | None = None):
+                   lib_path: str | None = None, drop_thr: int = 0, seed: int = 0):
     """See the module docstring. ``lib_path`` binds another build of the same
-    C source (the test suite uses it for deliberately broken copies)."""
+    C source (the test suite uses it for deliberately broken copies).
+    ``drop_thr`` in 1..255 applies dropout at probability drop_thr / 256 with
+    the generator seed ``seed`` (0 = no dropout)."""
     lib = _bind_lib(lib_path) if lib_path else _load()
     Q, K, V = _as_f32(q), _as_f32(k), _as_f32(v)
     if Q.ndim != 4 or K.ndim != 4 or V.ndim != 4:
@@ -94,10 +118,17 @@ def attention_fp64(q, k, v, causal: bool, scale: float, rows=None, threads: int 
         rows_ptr = rows_arr.ctypes.data
     O = np.empty((n_rows, dv), dtype=np.float64)
     lse = np.empty((n_rows,), dtype=np.float64)
-    rc = lib.attn_oracle_fp64(Q.ctypes.data, K.ctypes.data, V.ctypes.data,
-                              B, Hq, Hkv, Nq, Nkv, dqk, dv, int(bool(causal)),
-                              float(np.float32(scale)), rows_ptr, n_rows,
-                              O.ctypes.data, lse.ctypes.data, int(threads))
+    if drop_thr:
+        rc = lib.attn_oracle_dropout_fp64(Q.ctypes.data, K.ctypes.data, V.ctypes.data,
+                                          B, Hq, Hkv, Nq, Nkv, dqk, dv, int(bool(causal)),
+                                          float(np.float32(scale)), rows_ptr, n_rows,
+                                          O.ctypes.data, lse.ctypes.data, int(threads),
+                                          int(drop_thr), int(seed) & (2 ** 64 - 1))
+    else:
+        rc = lib.attn_oracle_fp64(Q.ctypes.data, K.ctypes.data, V.ctypes.data,
+                                  B, Hq, Hkv, Nq, Nkv, dqk, dv, int(bool(causal)),
+                                  float(np.float32(scale)), rows_ptr, n_rows,
+                                  O.ctypes.data, lse.ctypes.data, int(threads))
     if rc <= 0:
         raise ValueError("attn_oracle_fp64 failed with code %d" % rc)
     if rows is None:

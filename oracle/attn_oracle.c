@@ -29,6 +29,16 @@
  *   7. lse[b,h,i] = m + ln(l)  (natural log of sum_j exp(s_j); the pages only
  *      name "running max and normalizer", this is the reading used).
  *
+ * Dropout (attn_oracle_dropout_fp64; slide 54 puts it between softmax and
+ * ×V): p_j is replaced by p_j * keep_j / (1 - q), where q = thr / 256 is the
+ * drop probability and keep_j = [byte(b, h, i, j) >= thr]. lse stays that of
+ * the softmax before dropout. byte() is one byte of the counter-based
+ * generator Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random
+ * numbers: as easy as 1, 2, 3", SC'11), written here from that definition:
+ *   key  = (seed mod 2^32, seed / 2^32)
+ *   ctr  = (i, 2 * (j / 32) + (j / 4) mod 2, b * H_q + h, 0)
+ *   byte = bits 8t .. 8t+7 of output word w, w = (j / 8) mod 4, t = j mod 4.
+ *
  * Inputs are fp32 arrays (bf16 values widen to fp32 exactly), contiguous in
  * [B, H, N, d] order. All arithmetic is fp64. Rows are spread over POSIX
  * threads; nothing else is tuned.
@@ -47,9 +57,51 @@ typedef struct {
     const int64_t *rows; /* n_rows x 3 (b, h, i) or NULL for every row */
     int64_t n_rows;
     double *O, *lse;
+    int dropout;           /* apply dropout with threshold drop_thr */
+    uint32_t drop_thr;     /* 1 .. 255: drop when the element's byte < drop_thr */
+    uint64_t seed;
     int64_t next; /* shared row counter */
     pthread_mutex_t lock;
 } oracle_job;
+
+/* One Philox4x32 round: two 32x32 -> 64-bit products, the high halves xored
+ * with the other two words and the key, then the words permuted. */
+static void philox_round(uint32_t c[4], const uint32_t k[2]) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k[0];
+    const uint32_t n1 = (uint32_t)p1;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k[1];
+    const uint32_t n3 = (uint32_t)p0;
+    c[0] = n0; c[1] = n1; c[2] = n2; c[3] = n3;
+}
+
+/* Philox4x32-10: ten rounds, the key advanced by the Weyl constants between
+ * rounds. */
+void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+    uint32_t c[4] = {ctr[0], ctr[1], ctr[2], ctr[3]};
+    uint32_t k[2] = {key[0], key[1]};
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {
+            k[0] += 0x9E3779B9u;
+            k[1] += 0xBB67AE85u;
+        }
+        philox_round(c, k);
+    }
+    for (int w = 0; w < 4; ++w) out[w] = c[w];
+}
+
+/* keep_j / (1 - q) for element (b, h, i, j) */
+static double keep_factor(const oracle_job *J, int64_t b, int64_t h, int64_t i, int64_t j) {
+    const uint32_t key[2] = {(uint32_t)J->seed, (uint32_t)(J->seed >> 32)};
+    const uint32_t ctr[4] = {(uint32_t)i, (uint32_t)(2 * (j / 32) + (j / 4) % 2),
+                             (uint32_t)(b * J->Hq + h), 0u};
+    uint32_t out[4];
+    oracle_philox4x32_10(ctr, key, out);
+    const uint32_t byte = (out[(j / 8) % 4] >> (8 * (j % 4))) & 0xFFu;
+    if (byte < J->drop_thr) return 0.0;
+    return 256.0 / (256.0 - (double)J->drop_thr);
+}
 
 static void one_row(const oracle_job *J, int64_t b, int64_t h, int64_t i,
                     double *s, double *out_o, double *out_lse) {
@@ -79,8 +131,9 @@ static void one_row(const oracle_job *J, int64_t b, int64_t h, int64_t i,
     for (int64_t c = 0; c < J->dv; ++c) out_o[c] = 0.0;
     for (int64_t j = 0; j < n_keys; ++j) {
         const double p = s[j] / l;
+        const double pd = J->dropout ? p * keep_factor(J, b, h, i, j) : p;
         const float *v = vbase + j * J->dv;
-        for (int64_t c = 0; c < J->dv; ++c) out_o[c] += p * (double)v[c];
+        for (int64_t c = 0; c < J->dv; ++c) out_o[c] += pd * (double)v[c];
     }
     /* step 7 */
     *out_lse = m + log(l);
@@ -119,11 +172,12 @@ static void *worker(void *arg) {
  * `rows` (or, with rows == NULL, every (b, h, i) in row-major order, so that
  * n_rows must be B*H_q*N_q).
  */
-int attn_oracle_fp64(const float *Q, const float *K, const float *V,
-                     int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv,
-                     int64_t dqk, int64_t dv, int causal, float scale,
-                     const int64_t *rows, int64_t n_rows,
-                     double *O, double *lse, int n_threads) {
+static int run_oracle(const float *Q, const float *K, const float *V,
+                      int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv,
+                      int64_t dqk, int64_t dv, int causal, float scale,
+                      const int64_t *rows, int64_t n_rows,
+                      double *O, double *lse, int n_threads,
+                      int dropout, uint32_t drop_thr, uint64_t seed) {
     if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nkv < 1 || dqk < 1 || dv < 1) return -1;
     if (Hq % Hkv != 0) return -1;
     if (causal && Nq != Nkv) return -1;
@@ -141,6 +195,9 @@ int attn_oracle_fp64(const float *Q, const float *K, const float *V,
     J.scale = (double)scale;
     J.rows = rows; J.n_rows = n_rows;
     J.O = O; J.lse = lse;
+    J.dropout = dropout;
+    J.drop_thr = drop_thr;
+    J.seed = seed;
     J.next = 0;
     pthread_mutex_init(&J.lock, NULL);
 
@@ -167,4 +224,26 @@ int attn_oracle_fp64(const float *Q, const float *K, const float *V,
     free(tid);
     pthread_mutex_destroy(&J.lock);
     return failed ? -3 : started;
+}
+
+int attn_oracle_fp64(const float *Q, const float *K, const float *V,
+                     int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv,
+                     int64_t dqk, int64_t dv, int causal, float scale,
+                     const int64_t *rows, int64_t n_rows,
+                     double *O, double *lse, int n_threads) {
+    return run_oracle(Q, K, V, B, Hq, Hkv, Nq, Nkv, dqk, dv, causal, scale, rows, n_rows, O,
+                      lse, n_threads, 0, 0u, 0u);
+}
+
+/* As attn_oracle_fp64, with dropout at probability drop_thr / 256
+ * (1 <= drop_thr <= 255); -1 for a threshold outside that range. */
+int attn_oracle_dropout_fp64(const float *Q, const float *K, const float *V,
+                             int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv,
+                             int64_t dqk, int64_t dv, int causal, float scale,
+                             const int64_t *rows, int64_t n_rows,
+                             double *O, double *lse, int n_threads,
+                             uint32_t drop_thr, uint64_t seed) {
+    if (drop_thr < 1u || drop_thr > 255u) return -1;
+    return run_oracle(Q, K, V, B, Hq, Hkv, Nq, Nkv, dqk, dv, causal, scale, rows, n_rows, O,
+                      lse, n_threads, 1, drop_thr, seed);
 }

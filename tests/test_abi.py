@@ -241,3 +241,30 @@ def test_run_split_rejects_bad_arguments_before_launch():
         assert L.attn_fwd_run_split(plan, 16 + 2, 16, 16, 16, None, 0, 16, need, None) == ATTN_ERR_INVALID
     finally:
         attn.attn_fwd_destroy(plan)
+
+
+def test_dropout_probability_checked_before_any_hip_call():
+    L = attn.lib()
+    plan = attn.attn_fwd_create(1, 2, 2, 64, 128, True, 0.125)
+    P = ctypes.c_void_p(0x1000)
+    try:
+        for p in (1.0, 1.5, -0.1, float("nan")):
+            assert L.attn_fwd_run_dropout(plan, P, P, P, P, None, p, 1, None) == ATTN_ERR_INVALID
+        assert L.attn_fwd_run_dropout(None, P, P, P, P, None, 0.1, 1, None) == ATTN_ERR_INVALID
+        assert L.attn_fwd_run_dropout(plan, ctypes.c_void_p(0x1008), P, P, P, None, 0.1, 1,
+                                      None) == ATTN_ERR_INVALID
+    finally:
+        attn.attn_fwd_destroy(plan)
+
+
+def test_dropout_unsupported_for_wide_heads():
+    L = attn.lib()
+    p = AttnFwdParams()
+    p.B, p.H_q, p.H_kv, p.N, p.d, p.N_kv, p.d_v = 1, 2, 1, 16, 576, 64, 512
+    p.causal, p.scale, p.dtype = 0, 0.05, ATTN_BF16
+    plan = attn.attn_fwd_create_ex(p)
+    P = ctypes.c_void_p(0x1000)
+    try:
+        assert L.attn_fwd_run_dropout(plan, P, P, P, P, None, 0.1, 1, None) == ATTN_ERR_UNSUPPORTED
+    finally:
+        attn.attn_fwd_destroy(plan)

@@ -1,0 +1,94 @@
+"""Parity of attn_fwd_run_dropout with the fp64 oracle's dropout stage,
+through the C ABI: the keep decisions are integer work (bit-exact on both
+sides), so the same tolerances as without dropout apply to O (max |ΔO| <=
+2e-2) and to logsumexp (max |Δlse| <= 1e-2, the softmax before dropout)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from accelerator_programming_amd import attn
+from accelerator_programming_amd.inputs import C3, Workload, make_inputs, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = 2e-2
+TOL_LSE = 1e-2
+
+
+def run_drop(q, k, v, causal, scale, p_drop, seed):
+    B, Hq, N, _ = q.shape
+    o = torch.empty((B, Hq, N, v.shape[3]), dtype=q.dtype, device="cuda")
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device="cuda")
+    op = attn.AttnFwd(q, k, v, causal, scale, o)
+    try:
+        op.run_dropout(q, k, v, o, lse, p_drop=p_drop, seed=seed)
+    finally:
+        op.close()
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def check(o, lse, q, k, v, causal, scale, thr, seed, rows=None):
+    Oref, Lref, _ = oracle.attention_fp64(q, k, v, causal, scale, rows=rows, drop_thr=thr,
+                                          seed=seed)
+    if rows is None:
+        og, lg = o.float().cpu().numpy(), lse.cpu().numpy()
+    else:
+        r = torch.as_tensor(rows)
+        og = o[r[:, 0], r[:, 1], r[:, 2]].float().cpu().numpy()
+        lg = lse[r[:, 0], r[:, 1], r[:, 2]].cpu().numpy()
+    assert np.isfinite(og).all() and np.isfinite(lg).all()
+    dO = np.abs(og - Oref).max()
+    dL = np.abs(lg - Lref).max()
+    assert dO <= TOL_O, "max |dO| = %.3e" % dO
+    assert dL <= TOL_LSE, "max |dlse| = %.3e" % dL
+
+
+CASES = [
+    # B, Hq, Hkv, N, d, causal, dtype, p_drop, seed
+    (1, 4, 4, 300, 64, True, torch.bfloat16, 0.1, 1),
+    (2, 8, 2, 257, 128, True, torch.bfloat16, 0.25, (1 << 40) + 5),
+    (1, 2, 2, 200, 128, False, torch.bfloat16, 0.5, 3),
+    (1, 1, 1, 128, 64, False, torch.float32, 0.2, 4),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "N%d_d%d_%s_p%g" % (c[3], c[4], "causal" if c[5] else "full", c[7]))
+def test_dropout_parity(case):
+    B, Hq, Hkv, N, d, causal, dtype, p, seed = case
+    w = Workload("drop", B, Hq, Hkv, N, N, d, d, causal, dtype, 4242 + N)
+    q, k, v = make_inputs(w, "cuda")
+    o, lse = run_drop(q, k, v, causal, w.softmax_scale, p, seed)
+    check(o, lse, q, k, v, causal, w.softmax_scale, int(p * 256), seed)
+
+
+def test_dropout_full_size_sampled_rows():
+    q, k, v = make_inputs(C3, "cuda")
+    o, lse = run_drop(q, k, v, True, C3.softmax_scale, 0.1, 2024)
+    rows = sample_rows(C3, 24).numpy()
+    check(o, lse, q, k, v, True, C3.softmax_scale, int(0.1 * 256), 2024, rows=rows)
+
+
+def test_probability_below_one_step_is_plain_attention():
+    w = Workload("drop0", 1, 2, 2, 130, 130, 128, 128, True, torch.bfloat16, 77)
+    q, k, v = make_inputs(w, "cuda")
+    o1, l1 = run_drop(q, k, v, True, w.softmax_scale, 1.0 / 512, 9)
+    o2 = torch.empty_like(o1)
+    l2 = torch.empty_like(l1)
+    op = attn.AttnFwd(q, k, v, True, w.softmax_scale, o2)
+    op.run(q, k, v, o2, l2)
+    op.close()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_same_seed_repeats_and_other_seed_differs():
+    w = Workload("drop1", 1, 4, 4, 256, 256, 64, 64, False, torch.bfloat16, 78)
+    q, k, v = make_inputs(w, "cuda")
+    a, la = run_drop(q, k, v, False, w.softmax_scale, 0.3, 11)
+    b, lb = run_drop(q, k, v, False, w.softmax_scale, 0.3, 11)
+    c, lc = run_drop(q, k, v, False, w.softmax_scale, 0.3, 12)
+    assert torch.equal(a, b) and torch.equal(la, lb)
+    assert not torch.equal(a, c)
+    assert torch.equal(la, lc)  # logsumexp is that of the softmax before dropout
