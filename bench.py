@@ -29,6 +29,7 @@ PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12  # 2516.6
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 PROFILES = os.path.join(ROOT, "profiles")
 METRIC = "attention fwd TFLOP/s on 1 MI355X + % of bf16 MFMA peak (causal FLOPs /2)"
+DROPOUT_SEED = 1234
 
 
 def kernel_source_sha() -> str:
@@ -50,7 +51,7 @@ def gemm_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def kernel_name(w):
+def kernel_name(w, dropout=False):
     """The kernel the library launches for workload w (as rocprofv3 names it)."""
     causal = "true" if w.causal else "false"
     if w.decode:
@@ -58,8 +59,9 @@ def kernel_name(w):
     if w.dqk == 576:
         # V given as the leading columns of K takes the kernel that stages K only
         return "attn::attn_fwd_wide_%skernel<576, 512, %s>" % ("vk_" if w.v_from_k else "", causal)
-    return "attn::attn_fwd_kernel<%d, %s, %s>" % (
-        w.dqk, causal, "__bf16" if str(w.dtype) == "torch.bfloat16" else "float")
+    return "attn::attn_fwd_kernel<%d, %s, %s%s>" % (
+        w.dqk, causal, "__bf16" if str(w.dtype) == "torch.bfloat16" else "float",
+        ", true" if dropout else "")
 
 
 def traffic_for_current_kernel(workload_name: str, tag: str, sha=None):
@@ -75,7 +77,7 @@ def traffic_for_current_kernel(workload_name: str, tag: str, sha=None):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(w, q, k, v, target_s: float, threads: int):
+def cpu_baseline(w, q, k, v, target_s: float, threads: int, drop_thr: int = 0):
     """Time the oracle on a sample of rows sized for roughly target_s seconds."""
     import numpy as np
     import torch
@@ -96,7 +98,7 @@ def cpu_baseline(w, q, k, v, target_s: float, threads: int):
         rows = sample_rows(w, n, seed=123)
         t0 = time.perf_counter()
         _, _, used = oracle.attention_fp64(Q, K, V, w.causal, w.softmax_scale, rows=rows,
-                                           threads=threads)
+                                           threads=threads, drop_thr=drop_thr, seed=DROPOUT_SEED)
         return time.perf_counter() - t0, row_flops(rows), used, rows.shape[0]
 
     dt, fl, used, n = timed(max(threads * 4, 64))
@@ -143,6 +145,38 @@ def gemm_cpu_baseline(w, a, b, target_s: float, threads: int):
     }
 
 
+def settle(run, args):
+    """Run the untimed warmup steps and fix the timed step count. With the
+    defaults (-1): warm up for at least 5 steps and 0.3 s, then time at
+    least 20 steps and about 0.2 s of work. Returns (warmup, steps) used."""
+    import torch
+    if args.warmup >= 0:
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize()
+        warm, per_step = args.warmup, None
+    else:
+        warm = 0
+        t0 = time.perf_counter()
+        while warm < 5 or time.perf_counter() - t0 < 0.3:
+            run()
+            warm += 1
+            if warm % 5 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        per_step = (time.perf_counter() - t0) / warm
+    if args.steps > 0:
+        steps = args.steps
+    else:
+        if per_step is None:
+            t0 = time.perf_counter()
+            run()
+            torch.cuda.synchronize()
+            per_step = time.perf_counter() - t0
+        steps = max(20, int(0.2 / max(per_step, 1e-6)))
+    return warm, steps
+
+
 def gemm_main(args, w) -> int:
     """One step = one C = A·Bᵀ launch over the workload's full shape."""
     import torch
@@ -154,9 +188,7 @@ def gemm_main(args, w) -> int:
     a, b = make_gemm_inputs(w, "cuda")
     c = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
-        gemm.gemm_nt(a, b, out=c, stream=stream)
-    torch.cuda.synchronize()
+    args.warmup, args.steps = settle(lambda: gemm.gemm_nt(a, b, out=c, stream=stream), args)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -210,11 +242,17 @@ def gemm_main(args, w) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=-1,
+                    help="timed steps (default: at least 20 and at least 0.2 s of work)")
+    ap.add_argument("--warmup", type=int, default=-1,
+                    help="untimed steps first (default: at least 5 and at least 0.3 s of work, "
+                         "so that the clock has settled)")
     ap.add_argument("--config", default="C4",
                     help="workload C1..C5 (the metric is quoted on C4), D1/D2 (split-KV decode) "
                          "or G1/G2 (the bf16 GEMM of the projections)")
+    ap.add_argument("--dropout", type=float, default=0.0, metavar="P",
+                    help="attention workloads: run with dropout at probability P (steps of 1/256) "
+                         "through attn_fwd_run_dropout")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -257,11 +295,15 @@ def main() -> int:
         ws = torch.empty(attn.attn_fwd_split_workspace_bytes(op.plan, 0), dtype=torch.uint8,
                          device="cuda")
         op.run = lambda q, k, v, o, lse, stream=None: op.run_split(q, k, v, o, lse, 0, ws, stream)
+    drop_thr = int(args.dropout * 256)
+    if drop_thr:
+        if w.decode or w.dqk == 576:
+            print("bench.py: dropout is served by the d = 64 / 128 kernel only", file=sys.stderr)
+            return 2
+        op.run = lambda q, k, v, o, lse, stream=None: op.run_dropout(q, k, v, o, lse, args.dropout,
+                                                                     DROPOUT_SEED, stream)
     stream = torch.cuda.current_stream()
-
-    for _ in range(args.warmup):
-        op.run(q, k, v, o, lse, stream=stream)
-    torch.cuda.synchronize()
+    args.warmup, args.steps = settle(lambda: op.run(q, k, v, o, lse, stream=stream), args)
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -287,7 +329,7 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         threads = min(16, len(os.sched_getaffinity(0)))
-        cpu = cpu_baseline(w, q, k, v, args.cpu_seconds, threads)
+        cpu = cpu_baseline(w, q, k, v, args.cpu_seconds, threads, drop_thr)
 
     line = {
         "metric": METRIC,
@@ -306,13 +348,15 @@ def main() -> int:
                    "N_kv": w.Nkv, "d_qk": w.dqk, "d_v": w.dv, "causal": w.causal,
                    "gflop_per_step": round(flops / 1e9, 3), "parallelism": "single-gpu",
                    "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+                   "dropout": drop_thr / 256.0,
                    "outputs_finite": finite},
         "roofline": ({"bound": "mfma", "achieved": round(achieved, 2),
                       "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
                       "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                      "traffic": traffic_for_current_kernel(w.name, "attn_fwd_" + args.config),
+                      "traffic": traffic_for_current_kernel(
+                          w.name, "attn_fwd_" + args.config + ("_dropout" if drop_thr else "")),
                       "kernel_ms_avg": round(kern_avg_ms, 4),
-                      "kernel": kernel_name(w)} if not w.decode else
+                      "kernel": kernel_name(w, drop_thr > 0)} if not w.decode else
                      {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                       "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                       "traffic": traffic_for_current_kernel(w.name, "attn_split_" + args.config),
