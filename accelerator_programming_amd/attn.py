@@ -1,7 +1,8 @@
 """ctypes binding of the C ABI in include/attn_fwd.h (argument marshalling only).
 
 The names mirror the C entry points: ``attn_fwd_create``,
-``attn_fwd_create_ex``, ``attn_fwd_run``, ``attn_fwd_run_dropout``, ``attn_fwd_destroy``,
+``attn_fwd_create_ex``, ``attn_fwd_run``, ``attn_fwd_run_dropout``,
+``attn_fwd_run_rope``, ``attn_fwd_rope_workspace_bytes``, ``attn_rope_bf16``, ``attn_fwd_destroy``,
 ``attn_status_str`` and ``attn_fwd_plan_info``. Every step of the attention
 pass runs inside the HIP library; torch only provides device memory and the
 stream. If the library has not been built this module raises on first use:
@@ -75,6 +76,12 @@ def lib() -> ctypes.CDLL:
                                          ctypes.POINTER(ctypes.c_int32)]
         L.attn_fwd_run_dropout.restype = ctypes.c_int
         L.attn_fwd_run_dropout.argtypes = [P, P, P, P, P, P, ctypes.c_float, ctypes.c_uint64, P]
+        L.attn_rope_bf16.restype = ctypes.c_int
+        L.attn_rope_bf16.argtypes = [P, P, I64, I64, I64, I64, P, P, ctypes.c_float, P]
+        L.attn_fwd_rope_workspace_bytes.restype = I64
+        L.attn_fwd_rope_workspace_bytes.argtypes = [P]
+        L.attn_fwd_run_rope.restype = ctypes.c_int
+        L.attn_fwd_run_rope.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, I64, P]
         L.tile_gemm_bf16_nt.restype = ctypes.c_int
         L.tile_gemm_bf16_nt.argtypes = [I64, I64, I64, P, I64, P, I64, P, I64, P]
         _lib = L
@@ -226,6 +233,25 @@ class AttnFwd:
         if st != ATTN_OK:
             raise AttnError(st, "attn_fwd_run_dropout")
 
+    def run_rope(self, q, k, v, o, lse=None, base: float = 10000.0, k_rot=None,
+                 stream=None) -> None:
+        """attn_fwd_run_rope: attention of RoPE(Q), RoPE(K) against V. k_rot
+        (a device tensor of at least attn_fwd_rope_workspace_bytes bytes) is
+        allocated with torch when not given."""
+        import torch
+        need = int(lib().attn_fwd_rope_workspace_bytes(self.plan))
+        if need < 0:
+            raise AttnError(ATTN_ERR_UNSUPPORTED, "attn_fwd_run_rope")
+        if k_rot is None:
+            k_rot = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        s = stream if stream is not None else torch.cuda.current_stream()
+        st = lib().attn_fwd_run_rope(self.plan, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                     o.data_ptr(), lse.data_ptr() if lse is not None else None,
+                                     float(base), k_rot.data_ptr(),
+                                     k_rot.numel() * k_rot.element_size(), s.cuda_stream)
+        if st != ATTN_OK:
+            raise AttnError(st, "attn_fwd_run_rope")
+
     def split_count(self) -> int:
         return attn_fwd_split_count(self.plan)
 
@@ -275,3 +301,22 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None, with_ls
     finally:
         op.close()
     return o, lse
+
+
+def attn_rope_bf16(x, y=None, base: float = 10000.0, stream=None):
+    """RoPE of a [B, H, N, d] bf16 device tensor into y (new when None; y may
+    be x). Strides are passed through."""
+    import torch
+    if y is None:
+        y = torch.empty_like(x)
+    xs = (ctypes.c_int64 * 3)(*x.stride()[:3])
+    ys = (ctypes.c_int64 * 3)(*y.stride()[:3])
+    if x.stride(3) != 1 or y.stride(3) != 1:
+        raise ValueError("innermost stride must be 1")
+    s = stream if stream is not None else torch.cuda.current_stream()
+    B, H, N, d = x.shape
+    st = lib().attn_rope_bf16(x.data_ptr(), y.data_ptr(), B, H, N, d, xs, ys, float(base),
+                              s.cuda_stream)
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_rope_bf16")
+    return y

@@ -109,12 +109,33 @@ attn_status validate(const attn_fwd_params *in, attn_fwd_plan *out) {
     return ATTN_OK;
 }
 
-template <int D, bool CAUSAL, typename T, bool DROP = false>
+template <int D, bool CAUSAL, typename T, bool DROP = false, bool ROPE = false>
 hipError_t launch(const attn_fwd_plan *pl, const KernelArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL((attn::attn_fwd_kernel<D, CAUSAL, T, DROP>), dim3((uint32_t)pl->grid),
+    hipLaunchKernelGGL((attn::attn_fwd_kernel<D, CAUSAL, T, DROP, ROPE>), dim3((uint32_t)pl->grid),
                        dim3(pl->block), 0, stream, a);
     return hipGetLastError();
 }
+
+// RoPE launch over a [B, H, N, d] bf16 tensor (strides in elements, innermost 1)
+hipError_t launch_rope(const void *X, void *Y, int64_t B, int64_t H, int64_t N, int64_t d,
+                       const int64_t xs[3], const int64_t ys[3], double log2_base,
+                       hipStream_t stream) {
+    attn::RopeArgs r;
+    r.x = (const __bf16 *)X;
+    r.y = (__bf16 *)Y;
+    r.x_sb = xs[0]; r.x_sh = xs[1]; r.x_sn = xs[2];
+    r.y_sb = ys[0]; r.y_sh = ys[1]; r.y_sn = ys[2];
+    r.H = (int32_t)H;
+    r.N = (int32_t)N;
+    r.d = (int32_t)d;
+    r.chunks = B * H * N * (d / 8);
+    r.log2_base = log2_base;
+    const int64_t blocks = (r.chunks + 255) / 256;
+    hipLaunchKernelGGL(attn::rope_bf16_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream, r);
+    return hipGetLastError();
+}
+
+bool rope_base_ok(float base) { return std::isfinite(base) && base > 1.0f; }
 
 // Wide heads: V given as the first d_v columns of K's rows takes the kernel
 // that stages only K (512 threads); any other V takes the general one (the
@@ -168,6 +189,7 @@ KernelArgs make_args(const attn_fwd_plan *plan, const void *Q, const void *K, co
     a.drop_thr = 0;
     a.seed_lo = a.seed_hi = 0;
     a.drop_scale = 1.0f;
+    a.rope_log2_base = 0.0;
     return a;
 }
 
@@ -318,6 +340,64 @@ attn_status attn_fwd_run_dropout(const attn_fwd_plan *plan, const void *Q, const
         default:
             return ATTN_ERR_INVALID;
     }
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_rope_bf16(const void *X, void *Y, int64_t B, int64_t H, int64_t N, int64_t d,
+                           const int64_t x_strides[3], const int64_t y_strides[3], float base,
+                           void *stream) {
+    if (B < 0 || H < 0 || N < 0 || d < 8 || d % 8 != 0) return ATTN_ERR_INVALID;
+    if (!rope_base_ok(base)) return ATTN_ERR_INVALID;
+    if (B == 0 || H == 0 || N == 0) return ATTN_OK;
+    if (N >= ((int64_t)1 << 31) || d > 4096 || B * H * N * (d / 8) >= ((int64_t)1 << 40))
+        return ATTN_ERR_INVALID;
+    if (!X || !Y || !aligned16(X) || !aligned16(Y)) return ATTN_ERR_INVALID;
+    int64_t xs[3], ys[3];
+    for (int i = 0; i < 3; ++i) {
+        xs[i] = x_strides ? x_strides[i] : 0;
+        ys[i] = y_strides ? y_strides[i] : 0;
+    }
+    if (!fill_strides(xs, H, N, d, d, 8) || !fill_strides(ys, H, N, d, d, 8)) return ATTN_ERR_INVALID;
+    return launch_rope(X, Y, B, H, N, d, xs, ys, std::log2((double)base), (hipStream_t)stream) ==
+                   hipSuccess
+               ? ATTN_OK
+               : ATTN_ERR_HIP;
+}
+
+int64_t attn_fwd_rope_workspace_bytes(const attn_fwd_plan *plan) {
+    if (!plan || (plan->variant != V_D64_BF16 && plan->variant != V_D128_BF16)) return -1;
+    const attn_fwd_params &p = plan->p;
+    return p.B * p.H_kv * p.N_kv * p.d * 2;
+}
+
+attn_status attn_fwd_run_rope(const attn_fwd_plan *plan, const void *Q, const void *K, const void *V,
+                              void *O, float *lse, float base, void *k_rot, int64_t k_rot_bytes,
+                              void *stream) {
+    if (!plan || !Q || !K || !V || !O || !k_rot) return ATTN_ERR_INVALID;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(k_rot) ||
+        (lse && ((uintptr_t)lse & 3u)))
+        return ATTN_ERR_INVALID;
+    if (!rope_base_ok(base)) return ATTN_ERR_INVALID;
+    if (plan->variant != V_D64_BF16 && plan->variant != V_D128_BF16) return ATTN_ERR_UNSUPPORTED;
+    const attn_fwd_params &p = plan->p;
+    if (k_rot_bytes < attn_fwd_rope_workspace_bytes(plan)) return ATTN_ERR_INVALID;
+    const double log2_base = std::log2((double)base);
+    hipStream_t s = (hipStream_t)stream;
+    // K rotated once per kv head into the workspace ([B, H_kv, N_kv, d], contiguous)
+    int64_t ks[3] = {p.k_strides[0], p.k_strides[1], p.k_strides[2]};
+    int64_t rs[3] = {p.H_kv * p.N_kv * p.d, p.N_kv * p.d, p.d};
+    if (launch_rope(K, k_rot, p.B, p.H_kv, p.N_kv, p.d, ks, rs, log2_base, s) != hipSuccess)
+        return ATTN_ERR_HIP;
+    KernelArgs a = make_args(plan, Q, k_rot, V, O, lse);
+    a.k_sb = rs[0];
+    a.k_sh = rs[1];
+    a.k_sn = (int32_t)rs[2];
+    a.v_in_k = 0;
+    a.rope_log2_base = log2_base;
+    hipError_t e = p.d == 64 ? (p.causal ? launch<64, true, __bf16, false, true>(plan, a, s)
+                                         : launch<64, false, __bf16, false, true>(plan, a, s))
+                             : (p.causal ? launch<128, true, __bf16, false, true>(plan, a, s)
+                                         : launch<128, false, __bf16, false, true>(plan, a, s));
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

@@ -57,6 +57,7 @@
 #pragma once
 #include <type_traits>
 
+#include "rope.hpp"
 #include "tile.hpp"
 
 namespace attn {
@@ -76,6 +77,8 @@ struct KernelArgs {
     // 256 / (256 - drop_thr)
     uint32_t drop_thr, seed_lo, seed_hi;
     float drop_scale;
+    // RoPE of Q at load (kernels instantiated with ROPE only): log2(base)
+    double rope_log2_base;
 };
 
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
@@ -126,7 +129,7 @@ struct TileCfg {
 template <int N>
 using IC = std::integral_constant<int, N>;
 
-template <int D, bool CAUSAL, typename TIn, bool DROP = false>
+template <int D, bool CAUSAL, typename TIn, bool DROP = false, bool ROPE = false>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_kernel(const KernelArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
@@ -197,6 +200,9 @@ attn_fwd_kernel(const KernelArgs a) {
     for (int kc = 0; kc < NKC; ++kc) {
         u32x4 v = {0, 0, 0, 0};
         if (row < a.Nq) v = load8_bf16(Qp + (int64_t)row * a.q_sn + 16 * kc + 8 * g);
+        // RoPE on the way in: the chunk's four pairs start at pair 8kc + 4g
+        // of the row, whose position is its index
+        if constexpr (ROPE) v = rope_chunk(v, row, 8 * kc + 4 * g, D, a.rope_log2_base);
         qf[kc] = u32x4_as_bf16x8(v);
     }
 

@@ -124,6 +124,47 @@ attn_status attn_fwd_run_dropout(const attn_fwd_plan *plan, const void *Q, const
                                  uint64_t seed, void *stream);
 
 /*
+ * attn_rope_bf16 - rotary position embedding of a [B, H, N, d] bf16 tensor
+ * (the step before attention in the decoder chain of "CS149 L11: Programming
+ * Specialized Hardware", section 6; the pages' load-compute-store-finish
+ * example, "Distilling a 4.5 hour CUDA talk", section 12). Reading (the pages
+ * do not write the formula): the RoFormer rotation of interleaved pairs,
+ * pair k of the row at position n (its index) turned by
+ * theta = n * base^(-2k / d):
+ *   Y[2k] = X[2k] cos theta - X[2k+1] sin theta,
+ *   Y[2k+1] = X[2k] sin theta + X[2k+1] cos theta,
+ * in fp32 (the angle reduced in fp64), rounded to bf16.
+ * X, Y: device pointers, 16-byte aligned, (b, h, n) strides in elements as
+ * for attention (NULL or all-zero = contiguous), multiples of 8. Y may be X.
+ * d % 8 == 0, base finite and > 1 (else ATTN_ERR_INVALID); an empty tensor
+ * queues nothing. Asynchronous on `stream`.
+ */
+attn_status attn_rope_bf16(const void *X, void *Y, int64_t B, int64_t H, int64_t N, int64_t d,
+                           const int64_t x_strides[3], const int64_t y_strides[3], float base,
+                           void *stream);
+
+/*
+ * attn_fwd_rope_workspace_bytes - bytes of the workspace attn_fwd_run_rope
+ * needs for this plan (B * H_kv * N_kv * d bf16), or -1 if the plan's variant
+ * has no RoPE path (only bf16 with d = 64 or 128 has one).
+ */
+int64_t attn_fwd_rope_workspace_bytes(const attn_fwd_plan *plan);
+
+/*
+ * attn_fwd_run_rope - attention of RoPE(Q) and RoPE(K) (positions = row
+ * indices, as attn_rope_bf16 with `base`) against V. Q is rotated in
+ * registers as the kernel loads it; K is rotated once per kv head into the
+ * caller's workspace k_rot (k_rot_bytes >= attn_fwd_rope_workspace_bytes;
+ * 16-byte aligned; it may be K itself, which is then rotated in place) and
+ * the kernel reads K from there. O and logsumexp as for attn_fwd_run.
+ * ATTN_ERR_UNSUPPORTED for plans without a RoPE path; ATTN_ERR_INVALID for
+ * NULL or misaligned pointers, a short workspace or a bad base.
+ */
+attn_status attn_fwd_run_rope(const attn_fwd_plan *plan, const void *Q, const void *K,
+                              const void *V, void *O, float *lse, float base, void *k_rot,
+                              int64_t k_rot_bytes, void *stream);
+
+/*
  * Split-KV forward (few query rows per kv head, long key sequences: decode).
  * The keys of each kv head are cut into n_splits contiguous ranges; each
  * range's attention of all the group's query rows is computed separately and

@@ -268,3 +268,33 @@ def test_dropout_unsupported_for_wide_heads():
         assert L.attn_fwd_run_dropout(plan, P, P, P, P, None, 0.1, 1, None) == ATTN_ERR_UNSUPPORTED
     finally:
         attn.attn_fwd_destroy(plan)
+
+
+def test_rope_arguments_checked_before_any_hip_call():
+    L = attn.lib()
+    P = ctypes.c_void_p(0x1000)
+    assert L.attn_rope_bf16(P, P, 1, 1, 4, 12, None, None, 10000.0, None) == ATTN_ERR_INVALID  # d % 8
+    assert L.attn_rope_bf16(P, P, 1, 1, 4, 16, None, None, 1.0, None) == ATTN_ERR_INVALID  # base
+    assert L.attn_rope_bf16(P, P, 1, 1, 4, 16, None, None, float("inf"), None) == ATTN_ERR_INVALID
+    assert L.attn_rope_bf16(ctypes.c_void_p(0x1004), P, 1, 1, 4, 16, None, None, 1e4,
+                            None) == ATTN_ERR_INVALID
+    assert L.attn_rope_bf16(P, P, 0, 1, 4, 16, None, None, 1e4, None) == ATTN_OK  # empty
+    plan = attn.attn_fwd_create(1, 2, 2, 64, 128, True, 0.125)
+    try:
+        need = L.attn_fwd_rope_workspace_bytes(plan)
+        assert need == 1 * 2 * 64 * 128 * 2
+        assert L.attn_fwd_run_rope(plan, P, P, P, P, None, 1e4, P, need - 16,
+                                   None) == ATTN_ERR_INVALID
+        assert L.attn_fwd_run_rope(plan, P, P, P, P, None, 0.5, P, need, None) == ATTN_ERR_INVALID
+    finally:
+        attn.attn_fwd_destroy(plan)
+    p = AttnFwdParams()
+    p.B, p.H_q, p.H_kv, p.N, p.d = 1, 1, 1, 32, 64
+    p.causal, p.scale, p.dtype = 0, 0.125, ATTN_FP32
+    plan = attn.attn_fwd_create_ex(p)
+    try:
+        assert L.attn_fwd_rope_workspace_bytes(plan) == -1
+        assert L.attn_fwd_run_rope(plan, P, P, P, P, None, 1e4, P, 1 << 20,
+                                   None) == ATTN_ERR_UNSUPPORTED
+    finally:
+        attn.attn_fwd_destroy(plan)

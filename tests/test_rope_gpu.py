@@ -1,0 +1,112 @@
+"""RoPE on the GPU against the fp64 oracle, through the C ABI.
+
+attn_rope_bf16: the kernel rotates in fp32 (angle reduced in fp64) and rounds
+to bf16, so per element |y_gpu - y_ref| <= 2^-8 |y_ref| + 1e-4 (|x_2k| +
+|x_2k+1|) (one bf16 rounding plus the fp32 sine/cosine error).
+attn_fwd_run_rope: the attention tolerances (max |ΔO| <= 2e-2, max |Δlse| <=
+1e-2) against the oracle's attention of RoPE(Q), RoPE(K) (the rotated values
+reach the fp64 attention oracle through fp32, a 2^-24 relative step)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from accelerator_programming_amd import attn
+from accelerator_programming_amd.inputs import C4, Workload, make_inputs, sample_rows
+from oracle.rope import rope_fp64
+
+pytestmark = pytest.mark.gpu
+
+
+def check_rope(y, x, base):
+    X = x.float().cpu().numpy().astype(np.float64)
+    ref = rope_fp64(X, base)
+    got = y.float().cpu().numpy().astype(np.float64)
+    pair = np.abs(X[..., 0::2]) + np.abs(X[..., 1::2])
+    tol = 2.0 ** -8 * np.abs(ref) + 1e-4 * np.repeat(pair, 2, axis=-1)
+    bad = np.abs(got - ref) > tol
+    assert not bad.any(), "%d elements out of bound, worst %.3e" % (bad.sum(), np.abs(got - ref).max())
+
+
+def bf16(*shape, seed):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(shape, generator=g).to(torch.bfloat16).cuda()
+
+
+@pytest.mark.parametrize("shape,base", [((2, 3, 100, 64), 10000.0), ((1, 2, 16384, 128), 500000.0),
+                                        ((1, 1, 5, 8), 10000.0)])
+def test_rope_kernel(shape, base):
+    x = bf16(*shape, seed=sum(shape))
+    y = attn.attn_rope_bf16(x, base=base)
+    torch.cuda.synchronize()
+    check_rope(y, x, base)
+
+
+def test_rope_kernel_strided_and_in_place():
+    big = bf16(2, 4, 70, 128 + 64, seed=5)
+    x = big[:, 1:3, :, 32:32 + 128]          # strided view
+    x_copy = x.clone()
+    y = attn.attn_rope_bf16(x)
+    torch.cuda.synchronize()
+    check_rope(y, x_copy, 10000.0)
+    attn.attn_rope_bf16(x, x)                 # in place, through the view
+    torch.cuda.synchronize()
+    assert torch.equal(x, y)
+    assert torch.equal(big[:, 0], bf16(2, 4, 70, 128 + 64, seed=5)[:, 0])  # outside untouched
+
+
+def run_rope_attention(q, k, v, causal, scale, base):
+    B, Hq, N, _ = q.shape
+    o = torch.empty((B, Hq, N, v.shape[3]), dtype=q.dtype, device="cuda")
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device="cuda")
+    op = attn.AttnFwd(q, k, v, causal, scale, o)
+    try:
+        op.run_rope(q, k, v, o, lse, base=base)
+    finally:
+        op.close()
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def check_attention(o, lse, q, k, v, causal, scale, base, rows=None):
+    qr = rope_fp64(q, base)
+    kr = rope_fp64(k, base)
+    Oref, Lref, _ = oracle.attention_fp64(qr, kr, v, causal, scale, rows=rows)
+    if rows is None:
+        og, lg = o.float().cpu().numpy(), lse.cpu().numpy()
+    else:
+        r = torch.as_tensor(rows)
+        og = o[r[:, 0], r[:, 1], r[:, 2]].float().cpu().numpy()
+        lg = lse[r[:, 0], r[:, 1], r[:, 2]].cpu().numpy()
+    assert np.isfinite(og).all() and np.isfinite(lg).all()
+    assert np.abs(og - Oref).max() <= 2e-2, np.abs(og - Oref).max()
+    assert np.abs(lg - Lref).max() <= 1e-2, np.abs(lg - Lref).max()
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,causal,base", [
+    (2, 8, 2, 300, 128, True, 500000.0),
+    (1, 4, 4, 257, 64, False, 10000.0),
+    (1, 2, 1, 64, 128, True, 10000.0),
+])
+def test_rope_attention_parity(B, Hq, Hkv, N, d, causal, base):
+    w = Workload("rope", B, Hq, Hkv, N, N, d, d, causal, torch.bfloat16, 5151 + N)
+    q, k, v = make_inputs(w, "cuda")
+    k_before = k.clone()
+    o, lse = run_rope_attention(q, k, v, causal, w.softmax_scale, base)
+    assert torch.equal(k, k_before)  # K is rotated into the workspace, not in place
+    check_attention(o, lse, q, k, v, causal, w.softmax_scale, base)
+
+
+def test_rope_attention_full_size_sampled_rows():
+    q, k, v = make_inputs(C4, "cuda")
+    o, lse = run_rope_attention(q, k, v, True, C4.softmax_scale, 500000.0)
+    rows = sample_rows(C4, 16).numpy()
+    # the oracle rotates K on the CPU (the whole tensor) and Q for these rows
+    qr = rope_fp64(q, 500000.0)
+    kr = rope_fp64(k, 500000.0)
+    Oref, Lref, _ = oracle.attention_fp64(qr, kr, v, True, C4.softmax_scale, rows=rows)
+    r = torch.as_tensor(rows)
+    og = o[r[:, 0], r[:, 1], r[:, 2]].float().cpu().numpy()
+    lg = lse[r[:, 0], r[:, 1], r[:, 2]].cpu().numpy()
+    assert np.abs(og - Oref).max() <= 2e-2, np.abs(og - Oref).max()
+    assert np.abs(lg - Lref).max() <= 1e-2, np.abs(lg - Lref).max()
