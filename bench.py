@@ -36,7 +36,7 @@ def kernel_source_sha() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "accelerator_programming_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        if name.startswith("attn_fwd") or name == "tile.hpp":
+        if name.startswith("attn_fwd") or name in ("tile.hpp", "rope.hpp"):
             with open(os.path.join(csrc, name), "rb") as f:
                 h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -51,7 +51,7 @@ def gemm_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def kernel_name(w, dropout=False):
+def kernel_name(w, dropout=False, rope=False):
     """The kernel the library launches for workload w (as rocprofv3 names it)."""
     causal = "true" if w.causal else "false"
     if w.decode:
@@ -61,7 +61,7 @@ def kernel_name(w, dropout=False):
         return "attn::attn_fwd_wide_%skernel<576, 512, %s>" % ("vk_" if w.v_from_k else "", causal)
     return "attn::attn_fwd_kernel<%d, %s, %s%s>" % (
         w.dqk, causal, "__bf16" if str(w.dtype) == "torch.bfloat16" else "float",
-        ", true" if dropout else "")
+        ", true" if dropout else (", false, true" if rope else ""))
 
 
 def traffic_for_current_kernel(workload_name: str, tag: str, sha=None):
@@ -239,6 +239,59 @@ def gemm_main(args, w) -> int:
     return 0 if finite else 1
 
 
+def rope_main(args) -> int:
+    """R1: the standalone RoPE kernel over the Q of the long-sequence workload
+    ([1, 32, 16384, 128] bf16, base 500000): bound by HBM, each byte read and
+    written once."""
+    import torch
+
+    from accelerator_programming_amd import attn
+    from accelerator_programming_amd.inputs import C4, make_inputs
+
+    torch.cuda.set_device(0)
+    q, _, _ = make_inputs(C4, "cuda")
+    y = torch.empty_like(q)
+    base = args.rope or 500000.0
+    stream = torch.cuda.current_stream()
+    args.warmup, args.steps = settle(lambda: attn.attn_rope_bf16(q, y, base, stream), args)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        attn.attn_rope_bf16(q, y, base, stream)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / args.steps
+    nbytes = 2 * q.numel() * q.element_size()
+    gbs = nbytes / (kern_ms * 1e-3) / 1e9
+    line = {
+        "metric": "RoPE GB/s on 1 MI355X (bytes read + written)",
+        "value": round(nbytes / (wall / args.steps) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) inputs, resident in HBM)",
+        "config": {"workload": "R1_rope_B1_H32_N16384_d128", "base": base,
+                   "parallelism": "single-gpu", "bytes_per_step": nbytes},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_for_current_kernel("R1_rope_B1_H32_N16384_d128",
+                                                           "attn_rope_R1"),
+                     "kernel_ms_avg": round(kern_ms, 4), "kernel": "attn::rope_bf16_kernel"},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -253,6 +306,9 @@ def main() -> int:
     ap.add_argument("--dropout", type=float, default=0.0, metavar="P",
                     help="attention workloads: run with dropout at probability P (steps of 1/256) "
                          "through attn_fwd_run_dropout")
+    ap.add_argument("--rope", type=float, default=0.0, metavar="BASE",
+                    help="attention workloads: RoPE(Q), RoPE(K) with this base through "
+                         "attn_fwd_run_rope (R1 times the standalone RoPE kernel)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -283,6 +339,8 @@ def main() -> int:
 
     if args.config in GEMM_WORKLOADS:
         return gemm_main(args, GEMM_WORKLOADS[args.config])
+    if args.config == "R1":
+        return rope_main(args)
     w = WORKLOADS[args.config]
     torch.cuda.set_device(0)
     q, k, v = make_inputs(w, "cuda")
@@ -295,7 +353,18 @@ def main() -> int:
         ws = torch.empty(attn.attn_fwd_split_workspace_bytes(op.plan, 0), dtype=torch.uint8,
                          device="cuda")
         op.run = lambda q, k, v, o, lse, stream=None: op.run_split(q, k, v, o, lse, 0, ws, stream)
+    if args.rope:
+        if w.decode or w.dqk == 576 or w.dtype != torch.bfloat16:
+            print("bench.py: RoPE is served by the bf16 d = 64 / 128 kernel only", file=sys.stderr)
+            return 2
+        k_rot = torch.empty(attn.lib().attn_fwd_rope_workspace_bytes(op.plan), dtype=torch.uint8,
+                            device="cuda")
+        op.run = lambda q, k, v, o, lse, stream=None: op.run_rope(q, k, v, o, lse, args.rope,
+                                                                  k_rot, stream)
     drop_thr = int(args.dropout * 256)
+    if drop_thr and args.rope:
+        print("bench.py: --dropout and --rope are separate paths", file=sys.stderr)
+        return 2
     if drop_thr:
         if w.decode or w.dqk == 576:
             print("bench.py: dropout is served by the d = 64 / 128 kernel only", file=sys.stderr)
@@ -349,14 +418,17 @@ def main() -> int:
                    "gflop_per_step": round(flops / 1e9, 3), "parallelism": "single-gpu",
                    "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
                    "dropout": drop_thr / 256.0,
+                   "rope_base": args.rope or None,
                    "outputs_finite": finite},
         "roofline": ({"bound": "mfma", "achieved": round(achieved, 2),
                       "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
                       "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                       "traffic": traffic_for_current_kernel(
-                          w.name, "attn_fwd_" + args.config + ("_dropout" if drop_thr else "")),
+                          w.name, "attn_fwd_" + args.config + ("_dropout" if drop_thr else "")
+                          + ("_rope" if args.rope else "")),
                       "kernel_ms_avg": round(kern_avg_ms, 4),
-                      "kernel": kernel_name(w, drop_thr > 0)} if not w.decode else
+                      "kernel": ("attn::rope_bf16_kernel (K) + " if args.rope else "")
+                      + kernel_name(w, drop_thr > 0, args.rope > 0)} if not w.decode else
                      {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                       "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                       "traffic": traffic_for_current_kernel(w.name, "attn_split_" + args.config),
