@@ -128,9 +128,9 @@ hipError_t launch_rope(const void *X, void *Y, int64_t B, int64_t H, int64_t N, 
     r.H = (int32_t)H;
     r.N = (int32_t)N;
     r.d = (int32_t)d;
-    r.chunks = B * H * N * (d / 8);
+    r.row_blocks = (int32_t)((N + attn::ROPE_ROWS - 1) / attn::ROPE_ROWS);
     r.log2_base = log2_base;
-    const int64_t blocks = (r.chunks + 255) / 256;
+    const int64_t blocks = B * H * r.row_blocks;
     hipLaunchKernelGGL(attn::rope_bf16_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream, r);
     return hipGetLastError();
 }
@@ -349,7 +349,9 @@ attn_status attn_rope_bf16(const void *X, void *Y, int64_t B, int64_t H, int64_t
     if (B < 0 || H < 0 || N < 0 || d < 8 || d % 8 != 0) return ATTN_ERR_INVALID;
     if (!rope_base_ok(base)) return ATTN_ERR_INVALID;
     if (B == 0 || H == 0 || N == 0) return ATTN_OK;
-    if (N >= ((int64_t)1 << 31) || d > 4096 || B * H * N * (d / 8) >= ((int64_t)1 << 40))
+    // one workgroup per (b, h, 64 rows); a row's chunks fit one workgroup
+    if (N >= ((int64_t)1 << 31) || d > 2048 ||
+        B * H * ((N + attn::ROPE_ROWS - 1) / attn::ROPE_ROWS) >= ((int64_t)1 << 31))
         return ATTN_ERR_INVALID;
     if (!X || !Y || !aligned16(X) || !aligned16(Y)) return ATTN_ERR_INVALID;
     int64_t xs[3], ys[3];

@@ -20,19 +20,23 @@
 
 namespace attn {
 
-// cos and sin of t * base^(-2k / d), with log2_base = log2(base)
-__device__ __forceinline__ void rope_angle(int64_t t, int k, int d, double log2_base, float &c,
-                                           float &s) {
-    const double inv_freq = exp2(-(double)(2 * k) / (double)d * log2_base);
+// base^(-2k / d), with log2_base = log2(base)
+__device__ __forceinline__ double rope_inv_freq(int k, int d, double log2_base) {
+    return exp2(-(double)(2 * k) / (double)d * log2_base);
+}
+
+// cos and sin of t * inv_freq: the angle formed and reduced to [-pi, pi] in
+// fp64, then cos and sin in fp32
+__device__ __forceinline__ void rope_cos_sin(int64_t t, double inv_freq, float &c, float &s) {
     const double theta = (double)t * inv_freq;
     constexpr double kTwoPi = 6.283185307179586476925;
     const double red = theta - kTwoPi * rint(theta * (1.0 / kTwoPi));
     __sincosf((float)red, &s, &c);
 }
 
-// rotate the four pairs of a 16-byte bf16 chunk whose first element is
-// element 2 * k0 of its row (k0 = index of its first pair)
-__device__ __forceinline__ u32x4 rope_chunk(u32x4 v, int64_t t, int k0, int d, double log2_base) {
+// rotate the four pairs of a 16-byte bf16 chunk of the row at position t;
+// inv_freq[p] is the frequency of the chunk's pair p
+__device__ __forceinline__ u32x4 rope_chunk_f(u32x4 v, int64_t t, const double (&inv_freq)[4]) {
     u32x4 out;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
@@ -42,10 +46,18 @@ __device__ __forceinline__ u32x4 rope_chunk(u32x4 v, int64_t t, int k0, int d, d
         const bf16x2 xy = __builtin_bit_cast(bf16x2, word);
         const float x = (float)xy[0], y = (float)xy[1];
         float c, s;
-        rope_angle(t, k0 + p, d, log2_base, c, s);
+        rope_cos_sin(t, inv_freq[p], c, s);
         out[p] = pack_bf16x2(x * c - y * s, x * s + y * c);
     }
     return out;
+}
+
+// the same, with the frequencies of pairs k0 .. k0 + 3 formed here
+__device__ __forceinline__ u32x4 rope_chunk(u32x4 v, int64_t t, int k0, int d, double log2_base) {
+    double f[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) f[p] = rope_inv_freq(k0 + p, d, log2_base);
+    return rope_chunk_f(v, t, f);
 }
 
 struct RopeArgs {
@@ -53,25 +65,36 @@ struct RopeArgs {
     __bf16 *y;
     int64_t x_sb, x_sh, x_sn, y_sb, y_sh, y_sn;  // (b, h, n) strides in elements
     int32_t H, N, d;
-    int64_t chunks;  // B * H * N * d / 8
+    int32_t row_blocks;  // ceil(N / ROPE_ROWS)
     double log2_base;
 };
 
-// One lane per 16-byte chunk: load, rotate, store. Memory-bound: every byte
-// of X is read once and every byte of Y written once, in row order.
+constexpr int ROPE_ROWS = 64;  // rows of one (b, h) per workgroup
+
+// A workgroup rotates ROPE_ROWS rows of one (b, h); lane (slot, c) keeps the
+// frequencies of chunk c's four pairs and walks the rows slot, slot + S, ...
+// (S = 256 / chunks per row). Consecutive lanes touch consecutive 16-byte
+// chunks, so each row (and, for contiguous rows, the whole block) is one
+// coalesced run. Memory-bound: every byte of X is read once and every byte
+// of Y written once.
 __global__ void __launch_bounds__(256) rope_bf16_kernel(const RopeArgs a) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= a.chunks) return;
     const int cpr = a.d / 8;
-    const int c = (int)(i % cpr);
-    const int64_t r = i / cpr;
-    const int64_t n = r % a.N;
-    const int64_t bh = r / a.N;
+    const int slots = 256 / cpr;
+    const int c = threadIdx.x % cpr, slot = threadIdx.x / cpr;
+    if (slot >= slots) return;
+    const int rb = blockIdx.x % a.row_blocks;
+    const int64_t bh = blockIdx.x / a.row_blocks;
     const int64_t h = bh % a.H, b = bh / a.H;
-    const __bf16 *src = a.x + b * a.x_sb + h * a.x_sh + n * a.x_sn + 8 * c;
-    __bf16 *dst = a.y + b * a.y_sb + h * a.y_sh + n * a.y_sn + 8 * c;
-    const u32x4 v = *(const u32x4 *)src;
-    *(u32x4 *)dst = rope_chunk(v, n, 4 * c, a.d, a.log2_base);
+    double f[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) f[p] = rope_inv_freq(4 * c + p, a.d, a.log2_base);
+    const __bf16 *xb = a.x + b * a.x_sb + h * a.x_sh + 8 * c;
+    __bf16 *yb = a.y + b * a.y_sb + h * a.y_sh + 8 * c;
+    const int n_end = min(a.N, (rb + 1) * ROPE_ROWS);
+    for (int n = rb * ROPE_ROWS + slot; n < n_end; n += slots) {
+        const u32x4 v = *(const u32x4 *)(xb + (int64_t)n * a.x_sn);
+        *(u32x4 *)(yb + (int64_t)n * a.y_sn) = rope_chunk_f(v, n, f);
+    }
 }
 
 }  // namespace attn
