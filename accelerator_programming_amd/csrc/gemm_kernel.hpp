@@ -19,16 +19,18 @@
 // multiplied into the accumulators, and the next slabs stream in meanwhile.
 //
 // gfx950 mapping
-//  * 4 waves, one per SIMD; wave (wm, wn) owns C rows 128wm .. +127 and
-//    columns 128wn .. +127 of the tile as 4 x 4 accumulators of 32 x 32
-//    (256 accumulator registers; one wave per SIMD leaves 512).
+//  * 8 waves, two per SIMD, so that one wave's barrier and LDS waits are
+//    covered by the other's MFMAs; wave (wm, wn) owns C rows 128wm .. +127
+//    and columns 64wn .. +63 of the tile as 2 x 4 accumulators of 32 x 32
+//    (128 registers). With one wave per SIMD and 128 x 128 per wave the
+//    kernel ran 2-4 % slower on the projection shapes.
 //  * Cᵀ blocks are computed, Cᵀ = B·Aᵀ, with v_mfma_f32_32x32x16_bf16: the A
 //    operand is a 32-row slab of B, the B operand a 32-row slab of A, both
 //    read from LDS as 16 contiguous bytes per lane. A lane then holds one row
 //    of C and runs of four consecutive columns, which it stores as 8 bytes.
 //  * K steps of 32: A and B slabs (256 x 32 bf16 = 16 KB each) go through a
 //    four-stage LDS ring (128 KB) by LDS-DMA (buffer_load ... lds). Two copy
-//    groups (waves 0-1, waves 2-3) alternate: in step t the group t mod 2
+//    groups (waves 0-3, waves 4-7) alternate: in step t the group t mod 2
 //    copies the slabs of step t+3, one LDS-DMA after every second MFMA, and
 //    waits for them (vmcnt(0)) at the end of step t+1; one barrier per step.
 //  * LDS rows are 64 bytes (4 chunks of 16); chunk c of row r is stored at
@@ -57,8 +59,9 @@ struct GemmArgs {
 
 struct GemmCfg {
     static constexpr int BM = 256, BN = 256, BK = 32;
-    static constexpr int NWAVE = 4, NT = 64 * NWAVE;
-    static constexpr int WM = 128, WN = 128;       // per-wave C tile
+    static constexpr int NWAVE = 8, NT = 64 * NWAVE;
+    static constexpr int WM = 128, WN = 64;        // per-wave C tile
+    static constexpr int NB = WN / 32;             // 32-column blocks per wave
     static constexpr int NSTAGE = 4;
     static constexpr int SLAB = BM * BK;           // elements of one A (or B) slab
     static constexpr int STAGE_BYTES = 2 * SLAB * 2;
@@ -67,7 +70,7 @@ struct GemmCfg {
     // windows, so one step's A and B slabs are 32 windows, 16 per wave of the
     // copying group
     static constexpr int WIN_PER_SLAB = BM * BK * 2 / 1024;
-    static constexpr int DMA_PER_WAVE = 2 * WIN_PER_SLAB / 2;
+    static constexpr int DMA_PER_WAVE = 2 * WIN_PER_SLAB / (NWAVE / 2);
     static_assert(BM == BN, "A and B slabs share one shape");
     static_assert(LDS_BYTES <= 160 * 1024, "the ring must fit in LDS");
 };
@@ -75,7 +78,7 @@ struct GemmCfg {
 // physical 16-byte chunk of logical chunk c (0..3) in slab row r
 __device__ __forceinline__ int gemm_chunk(int r, int c) { return c ^ ((r >> 2) & 3); }
 
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_bf16_nt_kernel(const GemmArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
     using C = GemmCfg;
@@ -85,7 +88,7 @@ gemm_bf16_nt_kernel(const GemmArgs a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = w & 1, wn = w >> 1;
+    const int wm = w & 1, wn = w >> 1;  // wn 0..3
     const int l32 = lane & 31, g = lane >> 5;
 
     // ---- tile of this workgroup: XCD-contiguous runs, 8-row super-blocks ----
@@ -112,8 +115,8 @@ gemm_bf16_nt_kernel(const GemmArgs a) {
     const uint32_t abytes = ((uint32_t)(rows_a - 1) * (uint32_t)a.lda + (uint32_t)a.K) * 2u;
     const uint32_t bbytes = ((uint32_t)(rows_b - 1) * (uint32_t)a.ldb + (uint32_t)a.K) * 2u;
     const int n_steps = (a.K + BK - 1) / BK;
-    const int cw = w & 1;        // this wave's half of its group's windows
-    const int group = w >> 1;    // copy group: copies in steps t with t % 2 == group
+    const int cw = w & 3;        // this wave's quarter of its group's windows
+    const int group = w >> 2;    // copy group: copies in steps t with t % 2 == group
     // lane i of a window fills slab row 16 * win + i / 4 at physical chunk
     // i % 4, fetching the logical chunk the swizzle puts there
     const int dr = lane >> 2, dp = lane & 3;
@@ -121,7 +124,7 @@ gemm_bf16_nt_kernel(const GemmArgs a) {
     int kch[DPW];        // element offset in K of the fetched chunk
 #pragma unroll
     for (int u = 0; u < DPW; ++u) {
-        const int win = 2 * u + cw;                    // 0..31: A windows 0..15, B 16..31
+        const int win = 4 * u + cw;                    // 0..31: A windows 0..15, B 16..31
         const int row = 16 * (win & 15) + dr;
         const int c = gemm_chunk(row, dp);
         const int ld = win < 16 ? a.lda : a.ldb;
@@ -132,7 +135,7 @@ gemm_bf16_nt_kernel(const GemmArgs a) {
     // slabs of step t into stage t mod NS; K chunks past K get an offset past
     // every resource, so they read as zeros
     auto copy_one = [&](int t, int u) __attribute__((always_inline)) {
-        const int win = 2 * u + cw;
+        const int win = 4 * u + cw;
         const bool is_b = win >= 16;
         const uint32_t k0 = (uint32_t)t * BK;
         const uint64_t base = (is_b ? bbase : abase) + (uint64_t)k0 * 2u;
@@ -161,20 +164,26 @@ gemm_bf16_nt_kernel(const GemmArgs a) {
 
     // ---- fragment addresses: B rows (A operand) and A rows (B operand) ----
     // block i of this wave's 128 rows, k-substep kk: row 32i + l32, chunk 2kk + g
-    uint32_t fa[4][2], fb[4][2];
+    constexpr int NB = C::NB;
+    uint32_t fa[4][2], fb[NB][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             const int ra = C::WM * wm + 32 * i + l32;
-            const int rb = C::WN * wn + 32 * i + l32;
             fa[i][kk] = lds0 + (uint32_t)(ra * 64 + 16 * gemm_chunk(ra, 2 * kk + g));
+        }
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int rb = C::WN * wn + 32 * i + l32;
             fb[i][kk] = lds0 + (uint32_t)(C::SLAB * 2 + rb * 64 + 16 * gemm_chunk(rb, 2 * kk + g));
         }
 
-    f32x16 acc[4][4];  // acc[nb][mb]: Cᵀ block of columns 32nb.., rows 32mb..
+    f32x16 acc[NB][4];  // acc[nb][mb]: Cᵀ block of columns 32nb.., rows 32mb..
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NB; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -201,22 +210,21 @@ gemm_bf16_nt_kernel(const GemmArgs a) {
     // Two steps per iteration, so that whether this wave copies in a step is
     // known at compile time (COPIER). Past the last step the copy re-reads
     // the last step's slabs (the same bytes) into that step's stage.
-    bf16x8 xa[2][4], xb[2][4];
+    bf16x8 xa[2][4], xb[2][NB];
     auto load = [&](int set, uint32_t so, int kk) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            xb[set][i] = lds_read_b128(fb[i][kk] + so);
-            xa[set][i] = lds_read_b128(fa[i][kk] + so);
-        }
+        for (int i = 0; i < 4; ++i) xa[set][i] = lds_read_b128(fa[i][kk] + so);
+#pragma unroll
+        for (int i = 0; i < NB; ++i) xb[set][i] = lds_read_b128(fb[i][kk] + so);
     };
     auto mma = [&](int set, int tc, int kk, auto COPIER) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < NB; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 acc[i][j] = mfma_32x32x16(xb[set][i], xa[set][j], acc[i][j]);
                 if constexpr (decltype(COPIER)::value)
-                    if ((j & 1) == 1) copy_one(tc, 8 * kk + 2 * i + (j >> 1));
+                    if ((j & 1) == 1) copy_one(tc, 4 * kk + 2 * i + (j >> 1));
             }
     };
     auto step = [&](int t, auto COPIER) __attribute__((always_inline)) {
@@ -254,7 +262,7 @@ gemm_bf16_nt_kernel(const GemmArgs a) {
         if (row >= a.M) continue;
         __bf16 *crow = a.c + (int64_t)row * a.ldc;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < NB; ++i)
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const int col = n0 + C::WN * wn + 32 * i + acc_row(4 * rr, g);
