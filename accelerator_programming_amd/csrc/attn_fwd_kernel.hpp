@@ -15,8 +15,8 @@
 //    waves share only the K/V tiles in LDS.
 //  * Why two phase orders: on gfx950 a wave's VALU work does not overlap its
 //    own MFMAs, while the VALU and MFMA work of two waves on one SIMD do. In
-//    each period (one 64-key tile) wave p (role 0) runs its MFMAs first, P·V
-//    of the previous tile and the scores of this one, then its softmax; wave
+//    each period (one 64-key tile) wave p (role 0) runs its MFMAs first, the
+//    scores of this tile and P·V of the previous one, then its softmax; wave
 //    p + 4 (role 1) runs its softmax first, on scores it computed at the end
 //    of the previous period, then P·V and the next tile's scores. Each wave's
 //    exponentials run while its SIMD partner's MFMAs execute: compute never
@@ -467,7 +467,7 @@ attn_fwd_kernel(const KernelArgs a) {
             if (set_m) fix_m(snext);
         }
         // period T (T < n_live, a tile this wave computes): role 0 runs
-        // P·V(T-1), scores(T), softmax(T); role 1 softmax(T), P·V(T),
+        // scores(T), P·V(T-1), softmax(T); role 1 softmax(T), P·V(T),
         // scores(T+1). Copies by group T % 2: K(T+3) and V(T+2), one LDS-DMA
         // per four MFMAs of the period's two chains, so that the copy engine
         // is fed at its own pace instead of stalling a wave on a burst.
@@ -503,14 +503,16 @@ attn_fwd_kernel(const KernelArgs a) {
                     if ((f & 3) == 3) copy_job(PAR, T, DPC + (f >> 2), rk, rv);
             };
             if constexpr (R == 0) {
+                // scores first, so that their results have drained from the
+                // MFMA pipe (behind P·V) when the softmax reads them
+                f32x16 s[2];
+                scores(s, PAR, sc_hook);
                 if (P != 0 || T > 0) {
                     pv(pprev, (P + NS - 1) % NS * C::TILE * 2, pv_hook);
                 } else if constexpr (copier) {
 #pragma unroll
                     for (int j = 0; j < DPC; ++j) copy_job(PAR, T, j, rk, rv);
                 }
-                f32x16 s[2];
-                scores(s, PAR, sc_hook);
                 if (T == 0 && set_m) fix_m(s);
                 softmax(s, pprev, T, masked);
                 // P and l complete before the barrier: the softmax overlaps
