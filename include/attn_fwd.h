@@ -155,8 +155,8 @@ int64_t attn_fwd_rope_workspace_bytes(const attn_fwd_plan *plan);
  * indices, as attn_rope_bf16 with `base`) against V. Q is rotated in
  * registers as the kernel loads it; K is rotated once per kv head into the
  * caller's workspace k_rot (k_rot_bytes >= attn_fwd_rope_workspace_bytes;
- * 16-byte aligned; it may be K itself, which is then rotated in place) and
- * the kernel reads K from there. O and logsumexp as for attn_fwd_run.
+ * 16-byte aligned; it may be K itself, which is then rotated in place, but
+ * must not overlap Q, V or O) and the kernel reads K from there. O and logsumexp as for attn_fwd_run.
  * ATTN_ERR_UNSUPPORTED for plans without a RoPE path; ATTN_ERR_INVALID for
  * NULL or misaligned pointers, a short workspace or a bad base.
  */

@@ -84,12 +84,13 @@ def test_strided_operands_and_output():
 
 
 def test_k_zero_writes_zeros():
-    a = torch.empty((64, 0), dtype=torch.bfloat16, device="cuda")
-    b = torch.empty((32, 0), dtype=torch.bfloat16, device="cuda")
     out = torch.full((64, 32), 3.0, dtype=torch.bfloat16, device="cuda")
-    # zero-width tensors have no storage: hand the C ABI aligned stand-ins
-    gemm.tile_gemm_bf16_nt(64, 32, 0, out.data_ptr(), 0, out.data_ptr(), 0, out.data_ptr(), 32,
-                           torch.cuda.current_stream().cuda_stream)
+    # zero-width operands have no storage: hand the C ABI aligned stand-ins of
+    # their own (A and B must not overlap C), which it never reads
+    a_stub = torch.empty(8, dtype=torch.bfloat16, device="cuda")
+    b_stub = torch.empty(8, dtype=torch.bfloat16, device="cuda")
+    gemm.tile_gemm_bf16_nt(64, 32, 0, a_stub.data_ptr(), 0, b_stub.data_ptr(), 0, out.data_ptr(),
+                           32, torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     assert (out == 0).all()
 
