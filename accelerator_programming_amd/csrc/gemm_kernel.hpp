@@ -9,8 +9,8 @@
 // every workgroup owns a disjoint 256 x 256 tile of C and privately streams
 // the slabs of A and B it needs, so no two workgroups touch the same output
 // and nothing synchronizes between them; the tile is as large as the
-// accumulators of four waves can hold (output work grows with the tile's
-// area, input traffic with its perimeter). The same passage's super-blocked
+// workgroup's accumulators and LDS ring allow (output work grows with the
+// tile's area, input traffic with its perimeter). The same passage's super-blocked
 // launch order is used for L2 reuse: each XCD (own L2) takes a contiguous run
 // of tiles, walked in groups of 8 tile-rows so that neighbouring workgroups
 // share slabs of A and of B. The K loop is the inner loop of the
