@@ -289,15 +289,25 @@ class AttnFwd:
             pass
 
 
-def attention(q, k, v, causal: bool = False, scale: float | None = None, with_lse: bool = True):
-    """Allocate O (and lse) with torch and run the HIP kernel once."""
+def attention(q, k, v, causal: bool = False, scale: float | None = None, with_lse: bool = True,
+              dropout_p: float = 0.0, seed: int = 0, rope_base: float | None = None):
+    """Allocate O (and lse) with torch and run the HIP kernel once:
+    attn_fwd_run, or attn_fwd_run_dropout when dropout_p > 0, or
+    attn_fwd_run_rope when rope_base is given (not both)."""
     import torch
+    if dropout_p and rope_base:
+        raise ValueError("dropout and RoPE are separate entry points")
     B, Hq, N, _ = q.shape
     o = torch.empty((B, Hq, N, v.shape[3]), dtype=q.dtype, device=q.device)
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if with_lse else None
     op = AttnFwd(q, k, v, causal, scale, o)
     try:
-        op.run(q, k, v, o, lse)
+        if dropout_p:
+            op.run_dropout(q, k, v, o, lse, p_drop=dropout_p, seed=seed)
+        elif rope_base:
+            op.run_rope(q, k, v, o, lse, base=rope_base)
+        else:
+            op.run(q, k, v, o, lse)
     finally:
         op.close()
     return o, lse

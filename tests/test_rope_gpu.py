@@ -110,3 +110,18 @@ def test_rope_attention_full_size_sampled_rows():
     lg = lse[r[:, 0], r[:, 1], r[:, 2]].cpu().numpy()
     assert np.abs(og - Oref).max() <= 2e-2, np.abs(og - Oref).max()
     assert np.abs(lg - Lref).max() <= 1e-2, np.abs(lg - Lref).max()
+
+
+def test_attention_helper_routes_dropout_and_rope():
+    w = Workload("helper", 1, 4, 2, 150, 150, 128, 128, True, torch.bfloat16, 6060)
+    q, k, v = make_inputs(w, "cuda")
+    o_r, l_r = attn.attention(q, k, v, True, w.softmax_scale, rope_base=10000.0)
+    o_r2, l_r2 = run_rope_attention(q, k, v, True, w.softmax_scale, 10000.0)
+    assert torch.equal(o_r, o_r2) and torch.equal(l_r, l_r2)
+    o_d, l_d = attn.attention(q, k, v, True, w.softmax_scale, dropout_p=0.25, seed=9)
+    torch.cuda.synchronize()
+    O_ref, L_ref, _ = oracle.attention_fp64(q, k, v, True, w.softmax_scale, drop_thr=64, seed=9)
+    assert np.abs(o_d.float().cpu().numpy() - O_ref).max() <= 2e-2
+    assert np.abs(l_d.cpu().numpy() - L_ref).max() <= 1e-2
+    with pytest.raises(ValueError):
+        attn.attention(q, k, v, True, w.softmax_scale, dropout_p=0.1, rope_base=1e4)
