@@ -198,8 +198,11 @@ constexpr int32_t kMaxSplits = 64;  // the merge holds one split per lane
 
 bool split_supported(const attn_fwd_plan *pl) {
     const attn_fwd_params &p = pl->p;
+    // one 256-thread workgroup per (split, batch, kv head) and one per merged
+    // row (at most 64 per (batch, kv head)): each launch stays below 2^32
+    // work-items
     return (pl->variant == V_D64_BF16 || pl->variant == V_D128_BF16) && !p.causal &&
-           (p.H_q / p.H_kv) * p.N <= attn::SplitCfg<64>::ROWS;
+           (p.H_q / p.H_kv) * p.N <= attn::SplitCfg<64>::ROWS && (int64_t)p.B * p.H_kv <= (1 << 18);
 }
 
 // about two workgroups per CU (256 CUs), at least one 64-key tile per split
@@ -238,7 +241,7 @@ hipError_t launch_split(const attn_fwd_plan *pl, const KernelArgs &a, int32_t n,
                        stream, sa);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn::attn_split_merge<D>), dim3((uint32_t)((rows + 3) / 4)), dim3(256), 0, stream,
+    hipLaunchKernelGGL((attn::attn_split_merge<D>), dim3((uint32_t)rows), dim3(256), 0, stream,
                        (const float *)sa.opart, (const float *)sa.lpart, n, rows, a);
     return hipGetLastError();
 }

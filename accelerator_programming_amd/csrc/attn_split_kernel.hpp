@@ -106,16 +106,23 @@ attn_split_kernel(const SplitArgs sa) {
         }
     }
 
-    // ---- K/V copies: tile T (keys k_begin + 64 T ..) into stage T % 2 by
-    // wave T % 4: window u of a tensor covers rows ROWS_PER_DMA u .. of the
+    // ---- K/V copies: the tile of loop step T into stage T % 2 by wave
+    // T % 4: window u of a tensor covers rows ROWS_PER_DMA u .. of the
     // tile; lane i of a window lands at chunk i % CPR of row i / CPR and
     // fetches the global chunk the swizzle puts there; a buffer resource that
     // ends at the split's last key makes rows past it read as zeros. --------
+    // Loop step T works on tile phys(T) of the split: each workgroup starts
+    // at its own tile and wraps around, so that the workgroups, whose key
+    // ranges lie at equal power-of-two strides, do not all read the same
+    // offsets of their ranges at the same time (measured: +11 % bandwidth
+    // on 512 workgroups of 32 tiles). The softmax takes the keys in any order.
+    const int rot = n_tiles > 0 ? (int)(blockIdx.x % (uint32_t)n_tiles) : 0;
+    auto phys = [&](int T) { const int t = T + rot; return t >= n_tiles ? t - n_tiles : t; };
     const int dma_r = lane / C::CPR, dma_p = lane % C::CPR;
     auto copy_tile = [&](int T, int stage) __attribute__((always_inline)) {
         if (T >= n_tiles || (T & 3) != w) return;
         unsigned char *st = lds + stage * C::STAGE_B;
-        const int key0 = k_begin + T * TK;
+        const int key0 = k_begin + phys(T) * TK;
         const int rem = k_end - key0;  // >= 1
 #pragma unroll
         for (int is_v = 0; is_v < 2; ++is_v) {
@@ -157,7 +164,7 @@ attn_split_kernel(const SplitArgs sa) {
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc) sacc = mfma_32x32x16(kf[kc], qf[kc], sacc);
         // mask keys past the split's end, scale to base 2
-        const int key0 = k_begin + T * TK + 32 * kh;
+        const int key0 = k_begin + phys(T) * TK + 32 * kh;
         float t[16];
         float tmax = -INFINITY;
 #pragma unroll
@@ -254,46 +261,67 @@ attn_split_kernel(const SplitArgs sa) {
 #endif
 }
 
-// Merge of the splits, one wave per (b, h, i) row: lane s < n_splits holds
-// split s's logsumexp; lse = ln Σ exp(lse_s) (largest term factored out);
-// O = Σ_s exp(lse_s - lse) O_s, each lane D / 64 columns.
+// Merge of the splits, one workgroup per (b, h, i) row. Every thread loads
+// its share of the splits' partial rows at once (thread t: columns
+// 4 (t % (D/4)) .. + 3 of splits t / (D/4), + 256 / (D/4), ...), while wave 0
+// forms the weights from the splits' logsumexps: lse = ln Σ_s exp(lse_s)
+// (largest term factored out), w_s = exp(lse_s - lse); then each thread sums
+// w_s O_s over its splits and the split slots are added through LDS. One
+// memory round trip per row, whatever the split count.
 template <int D>
 __global__ void __launch_bounds__(256) attn_split_merge(const float *__restrict__ opart,
                                                         const float *__restrict__ lpart, int32_t n_splits,
                                                         int64_t n_rows, KernelArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= n_rows) return;
-    const float ls = lane < n_splits ? lpart[(int64_t)lane * n_rows + row] : -INFINITY;
-    float mxv = ls;
+    constexpr int CG = D / 4;         // float4 column groups of a row
+    constexpr int SLOTS = 256 / CG;   // split slots
+    constexpr int PER = 64 / SLOTS;   // splits per slot (at most 64 splits)
+    __shared__ float wsh[64];
+    __shared__ f32x4 red[SLOTS][CG];
+    const int t = threadIdx.x;
+    const int c = t % CG, j = t / CG;
+    const int64_t row = blockIdx.x;
+    f32x4 v[PER];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mxv = fmaxf(mxv, __shfl_xor(mxv, off));
-    const float mref = (mxv == -INFINITY) ? 0.f : mxv;
-    const float wgt = lane < n_splits ? exp2_hw((ls - mref) * 1.4426950408889634f) : 0.f;
-    float sum = wgt;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
-    const float inv = sum > 0.f ? 1.0f / sum : 0.f;
-    constexpr int CPL = D / 64;  // columns per lane
-    float acc[CPL];
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) acc[j] = 0.f;
-    for (int s = 0; s < n_splits; ++s) {
-        const float ws = __shfl(wgt, s) * inv;
-        const float *src = opart + ((int64_t)s * n_rows + row) * D;
-        if (ws != 0.f) {
-#pragma unroll
-            for (int j = 0; j < CPL; ++j) acc[j] += ws * src[CPL * lane + j];
-        }
+    for (int i = 0; i < PER; ++i) {
+        const int s = j + SLOTS * i;
+        v[i] = s < n_splits ? *(const f32x4 *)(opart + ((int64_t)s * n_rows + row) * D + 4 * c)
+                            : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    // row -> (b, h, i)
-    const int64_t i = row % a.Nq, bh = row / a.Nq;
-    const int64_t h = bh % a.Hq, b = bh / a.Hq;
-    __bf16 *orow = (__bf16 *)a.o + b * a.o_sb + h * a.o_sh + i * a.o_sn;
+    if (t < 64) {
+        const float ls = t < n_splits ? lpart[(int64_t)t * n_rows + row] : -INFINITY;
+        float mxv = ls;
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) orow[CPL * lane + j] = (__bf16)acc[j];
-    if (lane == 0 && a.lse) a.lse[row] = sum > 0.f ? mref + log2f(sum) * 0.69314718055994531f : -INFINITY;
+        for (int off = 32; off >= 1; off >>= 1) mxv = fmaxf(mxv, __shfl_xor(mxv, off));
+        const float mref = (mxv == -INFINITY) ? 0.f : mxv;
+        const float wgt = t < n_splits ? exp2_hw((ls - mref) * 1.4426950408889634f) : 0.f;
+        float sum = wgt;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+        const float inv = sum > 0.f ? 1.0f / sum : 0.f;
+        wsh[t] = wgt * inv;
+        if (t == 0 && a.lse) a.lse[row] = sum > 0.f ? mref + log2f(sum) * 0.69314718055994531f : -INFINITY;
+    }
+    __syncthreads();
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int s = j + SLOTS * i;
+        if (s < n_splits) acc += wsh[s] * v[i];
+    }
+    red[j][c] = acc;
+    __syncthreads();
+    if (t < CG) {
+        f32x4 o = red[0][t];
+#pragma unroll
+        for (int q = 1; q < SLOTS; ++q) o += red[q][t];
+        // row -> (b, h, i)
+        const int64_t i = row % a.Nq, bh = row / a.Nq;
+        const int64_t h = bh % a.Hq, b = bh / a.Hq;
+        __bf16 *orow = (__bf16 *)a.o + b * a.o_sb + h * a.o_sh + i * a.o_sn + 4 * t;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) orow[e] = (__bf16)o[e];
+    }
 #endif
 }
 

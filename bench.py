@@ -36,7 +36,7 @@ def kernel_source_sha() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "accelerator_programming_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        if name.startswith("attn_fwd") or name in ("tile.hpp", "rope.hpp"):
+        if name.startswith(("attn_fwd", "attn_split")) or name in ("tile.hpp", "rope.hpp"):
             with open(os.path.join(csrc, name), "rb") as f:
                 h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]

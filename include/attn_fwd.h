@@ -174,8 +174,9 @@ attn_status attn_fwd_run_rope(const attn_fwd_plan *plan, const void *Q, const vo
  * method, "Distilling a 4.5 hour CUDA talk", section 7: the running max and
  * normalizer carried across key tiles, here also across ranges).
  * Served problems: the plan's (d, d_v, dtype) is (64, 64, bf16) or
- * (128, 128, bf16), not causal, and (H_q / H_kv) * N <= 64 (all query rows
- * of a kv head fit one workgroup).
+ * (128, 128, bf16), not causal, (H_q / H_kv) * N <= 64 (all query rows
+ * of a kv head fit one workgroup) and B * H_kv <= 2^18 (the launches'
+ * work-items fit 32 bits).
  */
 
 /*

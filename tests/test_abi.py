@@ -215,7 +215,8 @@ def test_split_count_and_workspace_size():
     dict(causal=1, N=4096),                      # causal
     dict(N=32),                                  # 4 x 32 = 128 query rows per kv head
     dict(d=576, d_v=512, H_q=128, H_kv=1, N=1),  # wide heads
-], ids=["causal", "too_many_rows", "wide"])
+    dict(B=1 << 16, H_q=32, H_kv=8, N=1),         # 2^19 (batch, kv head) pairs
+], ids=["causal", "too_many_rows", "wide", "too_many_groups"])
 def test_split_path_declines_unserved_plans(kw):
     plan = split_plan(**kw)
     try:
