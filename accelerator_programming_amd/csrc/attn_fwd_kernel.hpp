@@ -81,6 +81,8 @@ struct KernelArgs {
     double rope_log2_base;
 };
 
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
 // easy as 1, 2, 3", SC'11): ten rounds of two 32x32 -> 64-bit products whose
 // high halves are xored with the other two words and the key, the key
@@ -94,8 +96,11 @@ __device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uin
             k0 += 0x9E3779B9u;
             k1 += 0xBB67AE85u;
         }
-        const uint32_t hi0 = __umulhi(0xD2511F53u, c[0]), lo0 = 0xD2511F53u * c[0];
-        const uint32_t hi1 = __umulhi(0xCD9E8D57u, c[2]), lo1 = 0xCD9E8D57u * c[2];
+        // the full 64-bit products: one v_mad_u64_u32 each, where a high and
+        // a low 32-bit multiply would take two slow-rate instructions
+        const uint64_t p0 = (uint64_t)c[0] * 0xD2511F53u, p1 = (uint64_t)c[2] * 0xCD9E8D57u;
+        const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+        const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
         const uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
         c[0] = n0;
         c[1] = lo1;
@@ -372,6 +377,7 @@ attn_fwd_kernel(const KernelArgs a) {
     // t = j mod 4 of output word (j / 8) mod 4. A lane's 16 keys of one
     // 32-key half are 8q + 4g + t (q, t < 4): one counter, all 16 bytes.
     // The kept values are scaled by 256 / (256 - drop_thr) at the end.
+    const i16x2 thr2 = {(short)a.drop_thr, (short)a.drop_thr};
     auto drop = [&](uint32_t (&pk)[2][8], int T) __attribute__((always_inline)) {
 #pragma unroll
         for (int js = 0; js < 2; ++js) {
@@ -380,11 +386,14 @@ attn_fwd_kernel(const KernelArgs a) {
             philox4x32_10(w, a.seed_lo, a.seed_hi);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                // elements 2j, 2j + 1: word j / 2, bytes 2 (j % 2) and 2 (j % 2) + 1
-                const uint32_t x = w[j >> 1] >> (16 * (j & 1));
-                const uint32_t lo = ((x & 0xFFu) >= a.drop_thr) ? 0x0000FFFFu : 0u;
-                const uint32_t hi = (((x >> 8) & 0xFFu) >= a.drop_thr) ? 0xFFFF0000u : 0u;
-                pk[js][j] &= lo | hi;
+                // elements 2j, 2j + 1: word j / 2, bytes 2 (j % 2) and 2 (j % 2) + 1,
+                // moved to the two 16-bit halves; byte - thr < 0 (drop) sets
+                // the half's sign, which the shift spreads over the half
+                const uint32_t sel = (j & 1) ? 0x0C030C02u : 0x0C010C00u;
+                const uint32_t bytes = __builtin_amdgcn_perm(0u, w[j >> 1], sel);
+                const i16x2 diff = __builtin_bit_cast(i16x2, bytes) - thr2;
+                const uint32_t drop_mask = __builtin_bit_cast(uint32_t, (i16x2)(diff >> (short)15));
+                pk[js][j] &= ~drop_mask;
             }
         }
     };
