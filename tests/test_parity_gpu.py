@@ -217,6 +217,9 @@ SPLIT = [
     (1, 4, 4, 1, 65, 128, 2),        # a one-key last range
     (1, 8, 8, 2, 100, 128, 8),       # more ranges than tiles: empty ranges
     (3, 6, 3, 3, 777, 64, 1),        # one range
+    (1, 8, 2, 2, 8192, 64, 64),      # d 64 at the most ranges: every merge slot
+    (2, 4, 4, 1, 5000, 64, 0),       # library count 64 over 79 tiles: empty ranges
+    (1, 4, 1, 3, 1000, 128, 5),      # ragged last tile inside a rotated range
 ]
 
 
