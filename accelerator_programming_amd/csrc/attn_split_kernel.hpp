@@ -209,7 +209,9 @@ attn_split_kernel(const SplitArgs sa) {
         if ((T & 3) == w) __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
         __syncthreads();  // tile T landed; every wave is done with tile T - 1
         copy_tile(T + C::NSTAGE - 1, stage == 0 ? C::NSTAGE - 1 : stage - 1);  // the stage of tile T - 1
-        tile_step(T, stage);
+        // a row block without query rows (group x N_q <= 32) keeps only its
+        // copy duty and the barriers
+        if (32 * rb < sa.rows) tile_step(T, stage);
         stage = stage == C::NSTAGE - 1 ? 0 : stage + 1;
     }
     __builtin_amdgcn_s_waitcnt(0x3f70);  // no copy outlives the loop

@@ -32,11 +32,18 @@ METRIC = "attention fwd TFLOP/s on 1 MI355X + % of bf16 MFMA peak (causal FLOPs 
 DROPOUT_SEED = 1234
 
 
-def kernel_source_sha() -> str:
+def kernel_source_sha(split: bool = False) -> str:
+    """Hash of the sources an attention profile was taken on: the host code,
+    the tile layer and RoPE, plus the main and wide kernels, or, for the
+    split-KV path, its own kernel and the main kernel header it includes."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "accelerator_programming_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        if name.startswith(("attn_fwd", "attn_split")) or name in ("tile.hpp", "rope.hpp"):
+        if split:
+            take = name in ("attn_fwd.hip", "attn_fwd_kernel.hpp", "attn_split_kernel.hpp", "tile.hpp", "rope.hpp")
+        else:
+            take = name.startswith("attn_fwd") or name in ("tile.hpp", "rope.hpp")
+        if take:
             with open(os.path.join(csrc, name), "rb") as f:
                 h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -431,7 +438,8 @@ def main() -> int:
                       + kernel_name(w, drop_thr > 0, args.rope > 0)} if not w.decode else
                      {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                       "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                      "traffic": traffic_for_current_kernel(w.name, "attn_split_" + args.config),
+                      "traffic": traffic_for_current_kernel(w.name, "attn_split_" + args.config,
+                                                                  kernel_source_sha(split=True)),
                       "kernel_ms_avg": round(kern_avg_ms, 4),
                       "tflops": round(achieved, 2),
                       "kernel": kernel_name(w)}),
