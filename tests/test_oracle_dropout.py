@@ -1,15 +1,53 @@
 """Pins of the oracle's dropout stage (test infrastructure only).
 
-Nothing here re-types the generator: the pins are what dropout and a
-counter-based generator must satisfy whatever their internals are -
-the keep rate, unbiasedness over seeds, the exact form of each kept value,
-independence of lse, determinism in (seed, b, h, i, j), and diffusion and
-injectivity of the Philox block."""
+Nothing here re-types the generator: the Philox4x32-10 block is held to the
+known-answer vectors published with the generator (Salmon, Moraes, Dror,
+Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC'11, and the test
+vectors of its reference distribution, Random123), and the rest are what
+dropout and a counter-based generator must satisfy whatever their internals
+are - the keep rate, unbiasedness over seeds, the exact form of each kept
+value, independence of lse, determinism in (seed, b, h, i, j), and diffusion
+and injectivity of the block. Deliberately broken copies of the generator
+(a wrong Weyl constant, a wrong multiplier, a missing round, the high and
+low product halves swapped) must each fail a pin."""
+import os
+import subprocess
+
 import numpy as np
 import pytest
 import torch
 
 import oracle
+
+# Published Philox4x32-10 known answers: (counter words, key words) -> output
+# words, all hexadecimal, word 0 first.
+PHILOX_KAT = [
+    ((0x00000000, 0x00000000, 0x00000000, 0x00000000), (0x00000000, 0x00000000),
+     (0x6627e8d5, 0xe169c58d, 0xbc57ac4c, 0x9b00dbd8)),
+    ((0xffffffff, 0xffffffff, 0xffffffff, 0xffffffff), (0xffffffff, 0xffffffff),
+     (0x408f276d, 0x41c83b0e, 0xa20bc7c6, 0x6d5451fd)),
+    ((0x243f6a88, 0x85a308d3, 0x13198a2e, 0x03707344), (0xa4093822, 0x299f31d0),
+     (0xd16cfe09, 0x94fdcceb, 0x5001e420, 0x24126ea1)),
+]
+
+
+def _philox_with(lib):
+    """philox4x32_10 bound to another build of the oracle's C source."""
+    def f(ctr, key):
+        c = np.ascontiguousarray(np.asarray(ctr, dtype=np.uint32).reshape(4))
+        k = np.ascontiguousarray(np.asarray(key, dtype=np.uint32).reshape(2))
+        out = np.empty(4, dtype=np.uint32)
+        lib.oracle_philox4x32_10(c.ctypes.data, k.ctypes.data, out.ctypes.data)
+        return out
+    return f
+
+
+def test_philox_known_answer_vectors(philox=None):
+    philox = philox or oracle.philox4x32_10
+    for ctr, key, want in PHILOX_KAT:
+        got = tuple(int(x) for x in philox(ctr, key))
+        assert got == want, "Philox4x32-10%s%s -> %s, published %s" % (
+            ctr, key, " ".join("%08x" % x for x in got), " ".join("%08x" % x for x in want))
 
 
 def inputs(B, Hq, Hkv, N, d, seed, Nkv=None, dv=None):
@@ -126,3 +164,33 @@ def test_philox_block_diffuses_single_bit_changes():
     flips = np.array(flips)
     assert 60 < flips.mean() < 68
     assert flips.min() > 30
+
+
+# --------------------------------------------------------------------------
+# Mutants of the generator: each must fail the known-answer pin.
+# --------------------------------------------------------------------------
+PHILOX_MUTANTS = {
+    "weyl_constant": ("k[1] += 0xBB67AE85u;", "k[1] += 0xBB67AE86u;"),
+    "multiplier": ("(uint64_t)0xD2511F53u * c[0]", "(uint64_t)0xD2511F57u * c[0]"),
+    "nine_rounds": ("for (int r = 0; r < 10; ++r) {\n        if (r > 0)",
+                    "for (int r = 0; r < 9; ++r) {\n        if (r > 0)"),
+    "halves_swapped": ("const uint32_t n1 = (uint32_t)p1;", "const uint32_t n1 = (uint32_t)(p1 >> 16);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PHILOX_MUTANTS))
+def test_known_answers_catch_generator_mutant(name, tmp_path):
+    import ctypes
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "attn_oracle.c")).read()
+    old, new = PHILOX_MUTANTS[name]
+    assert src.count(old) == 1, "mutation anchor not found: " + old
+    path_c = tmp_path / ("mut_%s.c" % name)
+    path_c.write_text(src.replace(old, new))
+    path_so = tmp_path / ("libmut_%s.so" % name)
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-o",
+                    str(path_so), str(path_c), "-lm"], check=True)
+    lib = ctypes.CDLL(str(path_so))
+    lib.oracle_philox4x32_10.restype = None
+    lib.oracle_philox4x32_10.argtypes = [ctypes.c_void_p] * 3
+    with pytest.raises(AssertionError):
+        test_philox_known_answer_vectors(_philox_with(lib))
