@@ -203,13 +203,45 @@ class AttnFwd:
     def info(self) -> dict:
         return attn_fwd_plan_info(self.plan)
 
+    def check(self, q, k, v, o, lse, where: str) -> None:
+        """Raise ValueError unless the tensors are device tensors with the
+        dtype, shapes and strides this plan was made for (the kernels index
+        memory from the plan, so a smaller tensor would be read or written
+        out of bounds), and lse (when given) is [B, H_q, N] contiguous fp32."""
+        import torch
+        p = self.params
+        dt = torch.bfloat16 if p.dtype == ATTN_BF16 else torch.float32
+        want = {
+            "q": ((p.B, p.H_q, p.N, p.d), tuple(p.q_strides)),
+            "k": ((p.B, p.H_kv, p.N_kv, p.d), tuple(p.k_strides)),
+            "v": ((p.B, p.H_kv, p.N_kv, p.d_v), tuple(p.v_strides)),
+            "o": ((p.B, p.H_q, p.N, p.d_v), tuple(p.o_strides)),
+        }
+        for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+            shape, strides = want[name]
+            if not isinstance(t, torch.Tensor) or not t.is_cuda:
+                raise ValueError("%s: %s must be a device tensor" % (where, name))
+            if t.dtype != dt:
+                raise ValueError("%s: %s has dtype %s, the plan was made for %s"
+                                 % (where, name, t.dtype, dt))
+            # a stride of a size-1 dimension never moves an address
+            if tuple(t.shape) != shape or any(
+                    n > 1 and st != want_st
+                    for n, st, want_st in zip(t.shape, t.stride(), strides + (1,))):
+                raise ValueError("%s: %s has shape %s strides %s, the plan was made for "
+                                 "shape %s strides %s" % (where, name, tuple(t.shape),
+                                                          tuple(t.stride()), shape,
+                                                          strides + (1,)))
+        if lse is not None:
+            if (not isinstance(lse, torch.Tensor) or not lse.is_cuda
+                    or lse.dtype != torch.float32 or not lse.is_contiguous()
+                    or tuple(lse.shape) != (p.B, p.H_q, p.N)):
+                raise ValueError("%s: lse must be a contiguous float32 device tensor of "
+                                 "shape %s" % (where, (p.B, p.H_q, p.N)))
+
     def run(self, q, k, v, o, lse=None, stream=None) -> None:
         import torch
-        for t in (q, k, v, o) + ((lse,) if lse is not None else ()):
-            if not t.is_cuda:
-                raise ValueError("attn_fwd_run needs device tensors")
-        if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
-            raise ValueError("lse must be a contiguous float32 tensor")
+        self.check(q, k, v, o, lse, "attn_fwd_run")
         s = stream if stream is not None else torch.cuda.current_stream()
         attn_fwd_run(self.plan, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                      lse.data_ptr() if lse is not None else None, s.cuda_stream)
@@ -221,11 +253,7 @@ class AttnFwd:
         """attn_fwd_run_dropout: dropout at probability floor(256 p_drop) / 256
         with the counter-based generator keyed by ``seed``."""
         import torch
-        for t in (q, k, v, o) + ((lse,) if lse is not None else ()):
-            if not t.is_cuda:
-                raise ValueError("attn_fwd_run_dropout needs device tensors")
-        if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
-            raise ValueError("lse must be a contiguous float32 tensor")
+        self.check(q, k, v, o, lse, "attn_fwd_run_dropout")
         s = stream if stream is not None else torch.cuda.current_stream()
         st = lib().attn_fwd_run_dropout(self.plan, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                         o.data_ptr(), lse.data_ptr() if lse is not None else None,
@@ -239,11 +267,14 @@ class AttnFwd:
         (a device tensor of at least attn_fwd_rope_workspace_bytes bytes) is
         allocated with torch when not given."""
         import torch
+        self.check(q, k, v, o, lse, "attn_fwd_run_rope")
         need = int(lib().attn_fwd_rope_workspace_bytes(self.plan))
         if need < 0:
             raise AttnError(ATTN_ERR_UNSUPPORTED, "attn_fwd_run_rope")
         if k_rot is None:
             k_rot = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        elif not k_rot.is_cuda or not k_rot.is_contiguous():
+            raise ValueError("attn_fwd_run_rope: k_rot must be a contiguous device tensor")
         s = stream if stream is not None else torch.cuda.current_stream()
         st = lib().attn_fwd_run_rope(self.plan, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                      o.data_ptr(), lse.data_ptr() if lse is not None else None,
@@ -261,16 +292,14 @@ class AttnFwd:
         attn_fwd_split_workspace_bytes bytes) is allocated with torch when
         not given."""
         import torch
-        for t in (q, k, v, o) + ((lse,) if lse is not None else ()):
-            if not t.is_cuda:
-                raise ValueError("attn_fwd_run_split needs device tensors")
-        if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
-            raise ValueError("lse must be a contiguous float32 tensor")
+        self.check(q, k, v, o, lse, "attn_fwd_run_split")
         need = attn_fwd_split_workspace_bytes(self.plan, n_splits)
         if need < 0:
             raise AttnError(ATTN_ERR_UNSUPPORTED, "attn_fwd_split_workspace_bytes")
         if workspace is None:
             workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        elif not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("attn_fwd_run_split: workspace must be a contiguous device tensor")
         s = stream if stream is not None else torch.cuda.current_stream()
         attn_fwd_run_split(self.plan, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                            lse.data_ptr() if lse is not None else None, n_splits,
@@ -317,12 +346,17 @@ def attn_rope_bf16(x, y=None, base: float = 10000.0, stream=None):
     """RoPE of a [B, H, N, d] bf16 device tensor into y (new when None; y may
     be x). Strides are passed through."""
     import torch
+    if not isinstance(x, torch.Tensor) or x.dim() != 4 or not x.is_cuda or x.dtype != torch.bfloat16:
+        raise ValueError("attn_rope_bf16: x must be a 4-D bf16 device tensor")
     if y is None:
         y = torch.empty_like(x)
-    xs = (ctypes.c_int64 * 3)(*x.stride()[:3])
-    ys = (ctypes.c_int64 * 3)(*y.stride()[:3])
+    if (not isinstance(y, torch.Tensor) or not y.is_cuda or y.dtype != torch.bfloat16
+            or tuple(y.shape) != tuple(x.shape)):
+        raise ValueError("attn_rope_bf16: y must be a bf16 device tensor of x's shape")
     if x.stride(3) != 1 or y.stride(3) != 1:
         raise ValueError("innermost stride must be 1")
+    xs = (ctypes.c_int64 * 3)(*x.stride()[:3])
+    ys = (ctypes.c_int64 * 3)(*y.stride()[:3])
     s = stream if stream is not None else torch.cuda.current_stream()
     B, H, N, d = x.shape
     st = lib().attn_rope_bf16(x.data_ptr(), y.data_ptr(), B, H, N, d, xs, ys, float(base),

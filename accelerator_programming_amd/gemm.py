@@ -31,8 +31,9 @@ def gemm_nt(a, b, out=None, stream=None):
     N = b.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
-    if out.shape != (M, N) or out.dtype != torch.bfloat16 or out.stride(1) != 1:
-        raise ValueError("out must be a [M, N] bf16 tensor with unit inner stride")
+    if (tuple(out.shape) != (M, N) or out.dtype != torch.bfloat16 or not out.is_cuda
+            or out.stride(1) != 1):
+        raise ValueError("out must be a [M, N] bf16 device tensor with unit inner stride")
     s = stream if stream is not None else torch.cuda.current_stream()
     tile_gemm_bf16_nt(M, N, K, a.data_ptr(), a.stride(0), b.data_ptr(), b.stride(0),
                       out.data_ptr(), out.stride(0), s.cuda_stream)

@@ -299,3 +299,24 @@ def test_rope_arguments_checked_before_any_hip_call():
                                    None) == ATTN_ERR_UNSUPPORTED
     finally:
         attn.attn_fwd_destroy(plan)
+
+
+def test_binding_rejects_host_tensors_before_the_c_abi():
+    # every run* method of the binding checks its tensors before it passes a
+    # pointer on: host memory never reaches a kernel
+    import torch
+    q = torch.zeros(1, 2, 64, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
+    o = torch.zeros_like(q)
+    op = attn.AttnFwd(q, k, k, False, 0.125, o)
+    try:
+        for call in (lambda: op.run(q, k, k, o),
+                     lambda: op.run_dropout(q, k, k, o, p_drop=0.5, seed=1),
+                     lambda: op.run_rope(q, k, k, o, k_rot=k),
+                     lambda: op.run_split(q, k, k, o, workspace=k)):
+            with pytest.raises(ValueError, match="device tensor"):
+                call()
+    finally:
+        op.close()
+    with pytest.raises(ValueError, match="device tensor"):
+        attn.attn_rope_bf16(q)
