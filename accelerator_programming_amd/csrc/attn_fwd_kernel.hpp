@@ -267,7 +267,9 @@ attn_fwd_kernel(const KernelArgs a) {
         uint32_t m0 = lds_k0 + (uint32_t)cw * 1024u;
         asm volatile("" : "+s"(m0));
         m0 += (is_v ? NS * C::TILE * 2 : 0) + stage_off + (uint32_t)(4 * u) * 1024u;
-        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+        // M0 (the LDS destination) is written inside the statement, and the
+        // DMA is followed by a wait state (see dma16_buf_to_lds)
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds\n\ts_nop 0"
                      :
                      : "s"(m0), "v"(is_v ? voff_v[u] : voff_k[u]), "s"(rsrc)
                      : "memory");
@@ -607,7 +609,10 @@ attn_fwd_kernel(const KernelArgs a) {
         l_row = xhalf_sum(l);
         if (exact) break;
         const bool bad = !(l_row <= kMaxL);  // also catches inf and NaN
-        if (lane == 0) wave_bad[w] = __builtin_amdgcn_ballot_w64(bad) != 0;
+        // the ballot runs in every lane (inside `lane == 0` it would see
+        // lane 0's row only); lane 0 then publishes the wave's verdict
+        const bool any_bad = __builtin_amdgcn_ballot_w64(bad) != 0;
+        if (lane == 0) wave_bad[w] = any_bad;
         lds_barrier();
         bool wg_bad = false;
 #pragma unroll

@@ -231,7 +231,10 @@ attn_fwd_wide_kernel(const KernelArgs a) {
     float l_row = xhalf_sum(l);
     // every wave holds the same rows' normalizers; decide once for the group
     __shared__ int wave_bad[C::NWAVE];
-    if (lane == 0) wave_bad[w] = __builtin_amdgcn_ballot_w64(!(l_row <= kMaxL)) != 0;
+    // the ballot runs in every lane (inside `lane == 0` it would see lane 0's
+    // row only); lane 0 then publishes the wave's verdict
+    const bool any_bad = __builtin_amdgcn_ballot_w64(!(l_row <= kMaxL)) != 0;
+    if (lane == 0) wave_bad[w] = any_bad;
     __syncthreads();
     bool wg_bad = false;
 #pragma unroll

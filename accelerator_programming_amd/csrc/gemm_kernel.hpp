@@ -148,7 +148,9 @@ gemm_bf16_nt_kernel(const GemmArgs a) {
         uint32_t m0v = lds0 + (uint32_t)(t % NS) * C::STAGE_BYTES;
         asm volatile("" : "+s"(m0v));
         m0v = __builtin_amdgcn_readfirstlane(m0v + (uint32_t)win * 1024u);
-        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+        // M0 (the LDS destination) is written inside the statement, and the
+        // DMA is followed by a wait state (see dma16_buf_to_lds in tile.hpp)
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds\n\ts_nop 0"
                      :
                      : "s"(m0v), "v"(off), "s"(rsrc)
                      : "memory");

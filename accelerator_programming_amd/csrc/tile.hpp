@@ -186,12 +186,18 @@ __device__ __forceinline__ bf16x8 vt_frag_at(uint32_t p, int kc) {
 // might alias (which would put a vmcnt(0) wait in front of those reads); the
 // caller owns the ordering: s_waitcnt vmcnt(0) and a barrier before any wave
 // reads the destination.
-// Nothing else in these kernels uses M0 (no LDS-size M0 on gfx9+, no
-// dynamic register indexing), so the assembly may set it freely.
+// M0 carries the LDS destination. The compiler reserves M0 (it never keeps a
+// value of its own there, and warns when M0 is named as a clobber), so the
+// statement writes it itself. The DMA reads M0 after it issues: with M0
+// bound as an operand instead, the compiler put the next DMA's M0 write
+// directly after the previous DMA and that DMA landed elsewhere in LDS
+// (wrong attention outputs on MI355X, different from run to run). So every
+// DMA statement here ends with a wait state (s_nop 0), and the next M0
+// write is always at least two instructions later.
 __device__ __forceinline__ void dma16_to_lds(const void *gptr, const void *lds_base) {
     const uint32_t addr =
         __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)lds_base);
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_nop 0"
                  :
                  : "s"(addr), "v"(gptr)
                  : "memory");
@@ -219,10 +225,10 @@ __device__ __forceinline__ u32x4 buffer_rsrc(const void *base, uint32_t bytes) {
 __device__ __forceinline__ void dma16_buf_to_lds(u32x4 rsrc, uint32_t voff, const void *lds_base) {
     const uint32_t addr =
         __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void *)lds_base);
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds\n\ts_nop 0"
                  :
                  : "s"(addr), "v"(voff), "s"(rsrc)
-                 : "memory", "m0");
+                 : "memory");
 }
 
 // Softmax work for one MFMA slot of the P·V / softmax overlap, as an

@@ -1,0 +1,210 @@
+"""Rows whose first 32 keys are far below their maximum: the exact-maxima
+pass of the fixed-reference softmax, against the fp64 oracle.
+
+The main kernel and both wide-head kernels take each row's exponent
+reference from its first 32 keys. The online softmax ("Distilling a 4.5 hour
+CUDA talk", section 7) carries a running maximum instead; the two agree in
+exact arithmetic, and the kernels keep that true for every input with a
+second pass: when some row's normalizer leaves [0, 2^32] (a later key
+outscored the first 32 by more than 32 log2 units) the workgroup finds the
+exact row maxima and recomputes. These inputs make that happen on purpose.
+
+Construction (seeded N(0, 1) inputs from the usual generator, then planted
+rows): q[b, h, i] = beta * k[b, g, j] for a key j >= 32 that row i sees, with
+beta a power of two (exact in bf16 and fp32). Then s_ij = beta |k_j|^2
+stands far above the row's other scores while |O_i| stays that of one V row,
+so the usual tolerances apply. A precondition check computes, in fp64 on the
+CPU, the gap between s_ij and the row's maximum over its first 32 visible
+keys in log2 units. Two kinds of planted rows:
+  * "over": gap >= 140, so 2^gap overflows fp32 in the first pass; only the
+    exact-maxima pass gives a finite, right answer. These rows sit at lanes
+    other than the first of their wave, so a wave-wide check that looked at
+    one lane would miss them.
+  * "mid": 40 <= gap < 120; the first pass is already exact here (its
+    reference only has to keep the exponentials finite), and the check
+    still sends the workgroup through the second pass.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from accelerator_programming_amd import attn
+from accelerator_programming_amd.inputs import Workload, make_inputs
+from oracle.rope import rope_fp64
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = 2e-2
+TOL_LSE = 1e-2
+LOG2E = 1.0 / math.log(2.0)
+
+
+def plant(q, k, plants):
+    """q[b, h, i, :] = beta * k[b, h // group, j, :] for each (b, h, i, j, beta)."""
+    group = q.shape[1] // k.shape[1]
+    for b, h, i, j, beta in plants:
+        q[b, h, i, :] = k[b, h // group, j, :] * beta
+    return q
+
+
+def gap_log2(q, k, scale, causal, b, h, i, j, base=None):
+    """(s_ij - max over the row's first 32 visible keys) in log2 units."""
+    group = q.shape[1] // k.shape[1]
+    Q = q[b, h].double().cpu().numpy()
+    K = k[b, h // group].double().cpu().numpy()
+    if base is not None:
+        Q, K = rope_fp64(Q, base), rope_fp64(K, base)
+    s = scale * (K @ Q[i])
+    first = s[: min(32, i + 1) if causal else 32]
+    return (s[j] - first.max()) * LOG2E
+
+
+def make(w, plants, base=None):
+    """plants: (b, h, i, j, beta, kind) with kind "over" or "mid"."""
+    q, k, v = make_inputs(w, "cpu")
+    if w.dtype == torch.float32:
+        # the kernel rounds fp32 inputs to bf16 on their way in; with a score
+        # of several hundred that rounding alone would move lse by ~0.3, so
+        # the planted key rows are made bf16-representable (exact on both
+        # sides); every other row keeps its full fp32 value
+        k = k.clone()
+        group = q.shape[1] // k.shape[1]
+        for b, h, i, j, beta, kind in plants:
+            k[b, h // group, j] = k[b, h // group, j].bfloat16().float()
+    q = plant(q.clone(), k, [p[:5] for p in plants])
+    for b, h, i, j, beta, kind in plants:
+        gap = gap_log2(q, k, w.softmax_scale, w.causal, b, h, i, j, base)
+        if kind == "over":
+            assert gap >= 140.0 and i % 32 != 0, "row (%d, %d, %d): gap %.1f" % (b, h, i, gap)
+        else:
+            assert 40.0 <= gap < 120.0, "row (%d, %d, %d): gap %.1f" % (b, h, i, gap)
+    q, k = q.cuda(), k.cuda()
+    v = k[..., : w.dv] if w.v_from_k else v.cuda()
+    return q, k, v
+
+
+def compare(o, lse, Oref, Lref):
+    og = o.float().cpu().numpy().astype(np.float64)
+    lg = lse.cpu().numpy().astype(np.float64)
+    assert np.isfinite(og).all() and np.isfinite(lg).all(), "non-finite output"
+    dO, dL = np.abs(og - Oref).max(), np.abs(lg - Lref).max()
+    assert dO <= TOL_O, "max |dO| = %.3e" % dO
+    assert dL <= TOL_LSE, "max |dlse| = %.3e" % dL
+
+
+def run(q, k, v, causal, scale, how="plain", **kw):
+    B, Hq, N, _ = q.shape
+    o = torch.empty((B, Hq, N, v.shape[3]), dtype=q.dtype, device="cuda")
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device="cuda")
+    op = attn.AttnFwd(q, k, v, causal, scale, o)
+    try:
+        if how == "plain":
+            op.run(q, k, v, o, lse)
+        elif how == "dropout":
+            op.run_dropout(q, k, v, o, lse, p_drop=kw["p_drop"], seed=kw["seed"])
+        elif how == "rope":
+            op.run_rope(q, k, v, o, lse, base=kw["base"])
+        elif how == "split":
+            op.run_split(q, k, v, o, lse, n_splits=kw.get("n_splits", 0))
+    finally:
+        op.close()
+    torch.cuda.synchronize()
+    return o, lse
+
+
+# (name, workload, planted (b, h, i, j, beta, kind))
+MAIN = [
+    # exactly one row of a 256-row query tile (rows 0 .. 255) trips the pass
+    ("d128_causal_one_row", Workload("fb", 1, 4, 2, 300, 300, 128, 128, True, torch.bfloat16, 901),
+     [(0, 1, 200, 150, 16.0, "over")]),
+    # outliers in the ragged last tile of the second query tile, and a mid one
+    ("d128_causal_ragged_tail", Workload("fb", 1, 2, 1, 300, 300, 128, 128, True, torch.bfloat16, 902),
+     [(0, 0, 299, 290, 16.0, "over"), (0, 1, 260, 40, 4.0, "mid")]),
+    ("d128_full_gqa", Workload("fb", 2, 4, 1, 200, 333, 128, 128, False, torch.bfloat16, 903),
+     [(1, 2, 7, 300, 16.0, "over"), (0, 0, 199, 33, 8.0, "mid")]),
+    ("d64_causal", Workload("fb", 1, 2, 2, 130, 130, 64, 64, True, torch.bfloat16, 904),
+     [(0, 0, 100, 40, 32.0, "over"), (0, 1, 129, 77, 8.0, "mid")]),
+    ("d64_full", Workload("fb", 2, 3, 1, 77, 1000, 64, 64, False, torch.bfloat16, 905),
+     [(1, 1, 76, 999, 32.0, "over"), (0, 2, 1, 500, 8.0, "mid")]),
+    ("d64_fp32_causal", Workload("fb", 1, 2, 1, 190, 190, 64, 64, True, torch.float32, 906),
+     [(0, 1, 189, 64, 32.0, "over")]),
+]
+
+
+@pytest.mark.parametrize("name,w,plants", MAIN, ids=[c[0] for c in MAIN])
+def test_fallback_main_kernel(name, w, plants):
+    q, k, v = make(w, plants)
+    o, lse = run(q, k, v, w.causal, w.softmax_scale)
+    Oref, Lref, _ = oracle.attention_fp64(q, k, v, w.causal, w.softmax_scale)
+    compare(o, lse, Oref, Lref)
+
+
+@pytest.mark.parametrize("d,causal", [(128, True), (64, False)])
+def test_fallback_with_dropout(d, causal):
+    w = Workload("fbd", 1, 2, 1, 260, 260, d, d, causal, torch.bfloat16, 907 + d)
+    plants = [(0, 1, 250, 100, 16.0 if d == 128 else 32.0, "over")]
+    q, k, v = make(w, plants)
+    o, lse = run(q, k, v, causal, w.softmax_scale, "dropout", p_drop=0.25, seed=77)
+    Oref, Lref, _ = oracle.attention_fp64(q, k, v, causal, w.softmax_scale, drop_thr=64, seed=77)
+    compare(o, lse, Oref, Lref)
+
+
+def test_fallback_with_rope():
+    # key j = i: RoPE turns q_i and k_i by the same angles, so the planted
+    # score survives the rotation. The kernel rounds RoPE(Q) and RoPE(K) to
+    # bf16 (RoPE's reading), which moves a score s by up to
+    # scale * sum_c |q'_c k'_c| * 2^-8 (two roundings of 2^-9); on a planted
+    # score of ~180 that is far above 1e-2, so the planted rows' lse gets that
+    # bound on top of the usual tolerance. Every other row, and O everywhere,
+    # keep the usual tolerances.
+    base = 10000.0
+    w = Workload("fbr", 1, 4, 2, 300, 300, 128, 128, True, torch.bfloat16, 909)
+    plants = [(0, 3, 120, 120, 16.0, "over"), (0, 0, 290, 290, 4.0, "mid")]
+    q, k, v = make(w, plants, base=base)
+    o, lse = run(q, k, v, True, w.softmax_scale, "rope", base=base)
+    qr, kr = rope_fp64(q, base), rope_fp64(k, base)
+    Oref, Lref, _ = oracle.attention_fp64(qr, kr, v, True, w.softmax_scale)
+    og = o.float().cpu().numpy().astype(np.float64)
+    lg = lse.cpu().numpy().astype(np.float64)
+    assert np.isfinite(og).all() and np.isfinite(lg).all(), "non-finite output"
+    assert np.abs(og - Oref).max() <= TOL_O, np.abs(og - Oref).max()
+    tol = np.full(Lref.shape, TOL_LSE)
+    group = w.Hq // w.Hkv
+    for b, h, i, j, beta, kind in plants:
+        tol[b, h, i] += w.softmax_scale * np.abs(qr[b, h, i] * kr[b, h // group, j]).sum() * 2.0 ** -8
+    assert (np.abs(lg - Lref) <= tol).all(), (np.abs(lg - Lref) - tol).max()
+
+
+WIDE = [
+    # V-in-K kernel (V the first 512 columns of K) and the general one (own V)
+    ("vk_full", Workload("fbw", 1, 3, 1, 64, 500, 576, 512, False, torch.bfloat16, 910, v_from_k=True),
+     [(0, 1, 5, 300, 8.0, "over"), (0, 2, 63, 499, 2.0, "mid")]),
+    ("vk_causal", Workload("fbw", 1, 2, 1, 200, 200, 576, 512, True, torch.bfloat16, 911, v_from_k=True),
+     [(0, 0, 150, 70, 8.0, "over")]),
+    ("v_full", Workload("fbw", 1, 2, 1, 40, 300, 576, 512, False, torch.bfloat16, 912),
+     [(0, 1, 39, 250, 8.0, "over"), (0, 0, 17, 100, 2.0, "mid")]),
+    ("v_causal", Workload("fbw", 1, 2, 2, 100, 100, 576, 512, True, torch.bfloat16, 913),
+     [(0, 1, 90, 45, 8.0, "over")]),
+]
+
+
+@pytest.mark.parametrize("name,w,plants", WIDE, ids=[c[0] for c in WIDE])
+def test_fallback_wide_kernels(name, w, plants):
+    q, k, v = make(w, plants)
+    o, lse = run(q, k, v, w.causal, w.softmax_scale)
+    Oref, Lref, _ = oracle.attention_fp64(q, k, v, w.causal, w.softmax_scale)
+    compare(o, lse, Oref, Lref)
+
+
+def test_split_path_with_an_outlier_key():
+    # the split-KV kernel carries a running maximum (no fixed reference): the
+    # same inputs must pass without any second pass
+    w = Workload("fbs", 1, 8, 2, 2, 3000, 128, 128, False, torch.bfloat16, 914)
+    plants = [(0, 5, 1, 2500, 16.0, "over"), (0, 0, 1, 40, 4.0, "mid")]
+    q, k, v = make(w, plants)
+    o, lse = run(q, k, v, False, w.softmax_scale, "split")
+    Oref, Lref, _ = oracle.attention_fp64(q, k, v, False, w.softmax_scale)
+    compare(o, lse, Oref, Lref)

@@ -263,3 +263,32 @@ def test_decode_workloads_full_size_sampled(name):
     q, k, v = make_inputs(w, "cuda")
     o, lse = run_split(q, k, v, w.softmax_scale, 0)
     compare(o, lse, q, k, v, False, w.softmax_scale, rows=sample_rows(w, 128))
+
+
+def test_binding_rejects_tensors_that_do_not_match_the_plan():
+    # the kernels index memory from the plan: a smaller or differently laid
+    # out tensor is refused in the binding, before any launch
+    w = Workload("chk", 1, 4, 2, 128, 128, 64, 64, True, torch.bfloat16, 3)
+    q, k, v = make_inputs(w, "cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((1, 4, 128), device="cuda")
+    op = attn.AttnFwd(q, k, v, True, w.softmax_scale, o)
+    try:
+        bad = {
+            "short q": (q[:, :, :64], k, v, o, lse),
+            "dtype": (q.float(), k, v, o, lse),
+            "strides": (q.transpose(1, 2).contiguous().transpose(1, 2), k, v, o, lse),
+            "lse shape": (q, k, v, o, lse[:, :2]),
+            "host o": (q, k, v, o.cpu(), lse),
+        }
+        for name, args in bad.items():
+            with pytest.raises(ValueError):
+                op.run(*args)
+            with pytest.raises(ValueError):
+                op.run_dropout(*args, p_drop=0.5, seed=1)
+    finally:
+        op.close()
+    with pytest.raises(ValueError):
+        attn.attn_rope_bf16(q.float())
+    with pytest.raises(ValueError):
+        attn.attn_rope_bf16(q, torch.empty_like(q)[:, :, :10])
