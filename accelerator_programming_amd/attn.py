@@ -2,7 +2,8 @@
 
 The names mirror the C entry points: ``attn_fwd_create``,
 ``attn_fwd_create_ex``, ``attn_fwd_run``, ``attn_fwd_run_dropout``,
-``attn_fwd_run_rope``, ``attn_fwd_rope_workspace_bytes``, ``attn_rope_bf16``, ``attn_fwd_destroy``,
+``attn_fwd_run_rope``, ``attn_fwd_rope_workspace_bytes``, ``attn_rope_bf16``,
+``attn_fwd_run_split``, ``attn_fwd_run_split_noalloc``, ``attn_fwd_destroy``,
 ``attn_status_str`` and ``attn_fwd_plan_info``. Every step of the attention
 pass runs inside the HIP library; torch only provides device memory and the
 stream. If the library has not been built this module raises on first use:
@@ -17,7 +18,9 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libattn_fwd.so")
 
-ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP, ATTN_ERR_NOMEM = range(5)
+(ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP, ATTN_ERR_NOMEM,
+ ATTN_ERR_TOO_LARGE) = range(6)
+ATTN_SPLIT_SCRATCH_BYTES = 16 * 1024 * 1024
 ATTN_BF16, ATTN_FP32 = 0, 1
 
 _I64x3 = ctypes.c_int64 * 3
@@ -69,6 +72,8 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd_split_workspace_bytes.argtypes = [P, ctypes.c_int32]
         L.attn_fwd_run_split.restype = ctypes.c_int
         L.attn_fwd_run_split.argtypes = [P, P, P, P, P, P, ctypes.c_int32, P, I64, P]
+        L.attn_fwd_run_split_noalloc.restype = ctypes.c_int
+        L.attn_fwd_run_split_noalloc.argtypes = [P, P, P, P, P, P, ctypes.c_int32, P]
         L.attn_fwd_plan_info.restype = ctypes.c_int
         L.attn_fwd_plan_info.argtypes = [P, ctypes.POINTER(I64), ctypes.POINTER(ctypes.c_int32),
                                          ctypes.POINTER(ctypes.c_int32),
@@ -135,6 +140,14 @@ def attn_fwd_run_split(plan: int, Q: int, K: int, V: int, O: int, lse: int | Non
                                   int(workspace_bytes), stream or None)
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd_run_split")
+
+
+def attn_fwd_run_split_noalloc(plan: int, Q: int, K: int, V: int, O: int, lse: int | None,
+                               n_splits: int, stream: int | None) -> None:
+    st = lib().attn_fwd_run_split_noalloc(plan, Q, K, V, O, lse or None, int(n_splits),
+                                          stream or None)
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_run_split_noalloc")
 
 
 def attn_fwd_destroy(plan: int | None) -> None:
@@ -305,6 +318,16 @@ class AttnFwd:
                            lse.data_ptr() if lse is not None else None, n_splits,
                            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                            s.cuda_stream)
+
+    def run_split_noalloc(self, q, k, v, o, lse=None, n_splits: int = 0, stream=None) -> None:
+        """The split-KV path through the library's static scratch (no device
+        allocation anywhere on the call)."""
+        import torch
+        self.check(q, k, v, o, lse, "attn_fwd_run_split_noalloc")
+        s = stream if stream is not None else torch.cuda.current_stream()
+        attn_fwd_run_split_noalloc(self.plan, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                   o.data_ptr(), lse.data_ptr() if lse is not None else None,
+                                   n_splits, s.cuda_stream)
 
     def close(self) -> None:
         if self.plan:

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
+#include <mutex>
 #include <new>
 
 #include "../../include/attn_fwd.h"
@@ -246,6 +247,41 @@ hipError_t launch_split(const attn_fwd_plan *pl, const KernelArgs &a, int32_t n,
     return hipGetLastError();
 }
 
+// ---- static scratch of attn_fwd_run_split_noalloc --------------------------
+// One buffer per GPU (each device holds its own copy of a __device__ array).
+// In host code `scratch` names a host-side stand-in, not device memory: the
+// device address is looked up with hipGetSymbolAddress once per device, with
+// that device current, and only that address is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[ATTN_SPLIT_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxDevices];
+
+// Device address of `scratch` on the device `stream` belongs to.
+hipError_t scratch_address(hipStream_t stream, void **out) {
+    int dev = -1;
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        int cur = -1;
+        e = hipGetDevice(&cur);
+        if (e != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        const hipError_t e2 = (cur != dev) ? hipSetDevice(cur) : hipSuccess;
+        if (e != hipSuccess) return e;
+        if (e2 != hipSuccess) return e2;
+        if (!p || ((uintptr_t)p & 255u)) return hipErrorInvalidValue;
+        g_scratch_addr[dev] = p;
+    }
+    *out = g_scratch_addr[dev];
+    return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -415,6 +451,7 @@ const char *attn_status_str(attn_status status) {
         case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED";
         case ATTN_ERR_HIP: return "ATTN_ERR_HIP";
         case ATTN_ERR_NOMEM: return "ATTN_ERR_NOMEM";
+        case ATTN_ERR_TOO_LARGE: return "ATTN_ERR_TOO_LARGE";
     }
     return "ATTN_ERR_UNKNOWN";
 }
@@ -446,6 +483,28 @@ attn_status attn_fwd_run_split(const attn_fwd_plan *plan, const void *Q, const v
     hipStream_t s = (hipStream_t)stream;
     const hipError_t e = plan->variant == V_D128_BF16 ? launch_split<128>(plan, a, n_splits, (float *)workspace, s)
                                                       : launch_split<64>(plan, a, n_splits, (float *)workspace, s);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status attn_fwd_run_split_noalloc(const attn_fwd_plan *plan, const void *Q, const void *K,
+                                       const void *V, void *O, float *lse, int32_t n_splits,
+                                       void *stream) {
+    // every argument check comes before the first HIP call
+    if (!plan || !Q || !K || !V || !O) return ATTN_ERR_INVALID;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) ||
+        (lse && ((uintptr_t)lse & 3u)))
+        return ATTN_ERR_INVALID;
+    if (!split_supported(plan)) return ATTN_ERR_UNSUPPORTED;
+    if (n_splits <= 0) n_splits = auto_splits(plan);
+    if (n_splits > kMaxSplits) return ATTN_ERR_INVALID;
+    const int64_t need = split_workspace(plan, n_splits);
+    if (need > ATTN_SPLIT_SCRATCH_BYTES) return ATTN_ERR_TOO_LARGE;
+    hipStream_t s = (hipStream_t)stream;
+    void *ws = nullptr;
+    if (scratch_address(s, &ws) != hipSuccess) return ATTN_ERR_HIP;
+    const KernelArgs a = make_args(plan, Q, K, V, O, lse);
+    const hipError_t e = plan->variant == V_D128_BF16 ? launch_split<128>(plan, a, n_splits, (float *)ws, s)
+                                                      : launch_split<64>(plan, a, n_splits, (float *)ws, s);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

@@ -24,7 +24,8 @@
  *   - logsumexp[b,h,i] = ln(sum_j exp(scale * q_i·k_j)) over unmasked keys.
  *   - All device buffers are owned by the caller, who keeps them alive until
  *     the work queued on the stream has finished. The library allocates no
- *     device memory.
+ *     device memory; its only device memory of its own is the static scratch
+ *     of attn_fwd_run_split_noalloc, part of the loaded code object.
  *   - Every function returns a status code; nothing throws or aborts across
  *     the ABI.
  */
@@ -44,7 +45,9 @@ typedef enum {
     ATTN_ERR_INVALID = 1,     /* malformed argument (sizes, strides, pointers) */
     ATTN_ERR_UNSUPPORTED = 2, /* well-formed but no kernel variant serves it */
     ATTN_ERR_HIP = 3,         /* the HIP runtime reported an error at launch */
-    ATTN_ERR_NOMEM = 4        /* host allocation of the plan failed */
+    ATTN_ERR_NOMEM = 4,       /* host allocation of the plan failed */
+    ATTN_ERR_TOO_LARGE = 5    /* the problem needs more scratch than the library's
+                                 static buffer holds (attn_fwd_run_split_noalloc) */
 } attn_status;
 
 typedef enum {
@@ -207,6 +210,31 @@ int64_t attn_fwd_split_workspace_bytes(const attn_fwd_plan *plan, int32_t n_spli
 attn_status attn_fwd_run_split(const attn_fwd_plan *plan, const void *Q, const void *K,
                                const void *V, void *O, float *lse, int32_t n_splits,
                                void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * attn_fwd_run_split_noalloc - attn_fwd_run_split for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. The per-range partial results go to a
+ * buffer the library keeps in static device memory, ATTN_SPLIT_SCRATCH_BYTES
+ * (16 MiB) per GPU, held by every GPU the library runs on until the process
+ * ends, instead of a caller workspace. Nothing is allocated: no hipMalloc,
+ * hipFree or allocating library routine. The first call on a device looks
+ * the buffer's address up on that device (the stream's device, or the
+ * current device for the NULL stream); later calls reuse it.
+ * Arguments as attn_fwd_run_split without the workspace. Returns
+ * ATTN_ERR_TOO_LARGE (before any HIP call) when
+ * attn_fwd_split_workspace_bytes(plan, n_splits) exceeds
+ * ATTN_SPLIT_SCRATCH_BYTES; the other argument errors as attn_fwd_run_split;
+ * ATTN_ERR_HIP when the buffer's address cannot be found or a launch fails.
+ * Every call on a GPU shares that GPU's buffer, which keeps the last call's
+ * contents (nothing in it needs clearing between calls): calls that overlap
+ * on one GPU - on other streams or from other threads - race, and the
+ * caller must order them.
+ */
+#define ATTN_SPLIT_SCRATCH_BYTES (16ll * 1024 * 1024)
+attn_status attn_fwd_run_split_noalloc(const attn_fwd_plan *plan, const void *Q, const void *K,
+                                       const void *V, void *O, float *lse, int32_t n_splits,
+                                       void *stream);
 
 /* attn_fwd_destroy - free a plan. NULL is accepted and ignored. */
 void attn_fwd_destroy(attn_fwd_plan *plan);

@@ -320,3 +320,35 @@ def test_binding_rejects_host_tensors_before_the_c_abi():
         op.close()
     with pytest.raises(ValueError, match="device tensor"):
         attn.attn_rope_bf16(q)
+
+
+def test_split_noalloc_rejects_bad_arguments_before_any_hip_call():
+    # these return before the library looks up its static scratch (no GPU here)
+    from accelerator_programming_amd.attn import ATTN_ERR_TOO_LARGE, ATTN_SPLIT_SCRATCH_BYTES
+    L = attn.lib()
+    plan = split_plan()
+    try:
+        assert L.attn_fwd_run_split_noalloc(None, 16, 16, 16, 16, None, 0, None) == ATTN_ERR_INVALID
+        assert L.attn_fwd_run_split_noalloc(plan, 16, None, 16, 16, None, 0, None) == ATTN_ERR_INVALID
+        assert L.attn_fwd_run_split_noalloc(plan, 16 + 2, 16, 16, 16, None, 0, None) == ATTN_ERR_INVALID
+        assert L.attn_fwd_run_split_noalloc(plan, 16, 16, 16, 16, 18, 0, None) == ATTN_ERR_INVALID
+        assert L.attn_fwd_run_split_noalloc(plan, 16, 16, 16, 16, None, 65, None) == ATTN_ERR_INVALID
+    finally:
+        attn.attn_fwd_destroy(plan)
+    # a plan the split path does not serve (causal)
+    plan = split_plan(causal=1, N=4096)
+    try:
+        assert L.attn_fwd_run_split_noalloc(plan, 16, 16, 16, 16, None, 0, None) == \
+            ATTN_ERR_UNSUPPORTED
+    finally:
+        attn.attn_fwd_destroy(plan)
+    # more partial results than the static buffer holds
+    plan = split_plan(B=64, N=1)
+    try:
+        need = attn.attn_fwd_split_workspace_bytes(plan, 64)
+        assert need > ATTN_SPLIT_SCRATCH_BYTES
+        assert L.attn_fwd_run_split_noalloc(plan, 16, 16, 16, 16, None, 64, None) == \
+            ATTN_ERR_TOO_LARGE
+        assert attn.attn_status_str(ATTN_ERR_TOO_LARGE) == "ATTN_ERR_TOO_LARGE"
+    finally:
+        attn.attn_fwd_destroy(plan)
