@@ -1,28 +1,34 @@
-"""Rows whose first 32 keys are far below their maximum: the exact-maxima
-pass of the fixed-reference softmax, against the fp64 oracle.
+"""Rows whose exponentials leave the range the first pass assumes: the
+exact-maxima pass, against the fp64 oracle.
 
-The main kernel and both wide-head kernels take each row's exponent
-reference from its first 32 keys. The online softmax ("Distilling a 4.5 hour
-CUDA talk", section 7) carries a running maximum instead; the two agree in
-exact arithmetic, and the kernels keep that true for every input with a
-second pass: when some row's normalizer leaves [0, 2^32] (a later key
-outscored the first 32 by more than 32 log2 units) the workgroup finds the
-exact row maxima and recomputes. These inputs make that happen on purpose.
+The online softmax ("Distilling a 4.5 hour CUDA talk", section 7) carries a
+running maximum. The main kernel (d 64 / 128) and both wide-head kernels
+replace it with a fixed exponent reference per row, the row's maximum over its
+first 32 keys; that gives the same O and lse in exact arithmetic and only has
+to keep the exponentials in range. When some row's normalizer leaves
+[0, 2^32] (a later key outscored the first 32 by more than 32 log2 units) the
+workgroup finds the exact row maxima and recomputes. These inputs make that
+happen on purpose.
 
 Construction (seeded N(0, 1) inputs from the usual generator, then planted
-rows): q[b, h, i] = beta * k[b, g, j] for a key j >= 32 that row i sees, with
-beta a power of two (exact in bf16 and fp32). Then s_ij = beta |k_j|^2
-stands far above the row's other scores while |O_i| stays that of one V row,
-so the usual tolerances apply. A precondition check computes, in fp64 on the
-CPU, the gap between s_ij and the row's maximum over its first 32 visible
-keys in log2 units. Two kinds of planted rows:
-  * "over": gap >= 140, so 2^gap overflows fp32 in the first pass; only the
-    exact-maxima pass gives a finite, right answer. These rows sit at lanes
-    other than the first of their wave, so a wave-wide check that looked at
-    one lane would miss them.
-  * "mid": 40 <= gap < 120; the first pass is already exact here (its
-    reference only has to keep the exponentials finite), and the check
-    still sends the workgroup through the second pass.
+rows, all exact in bf16):
+  * "over": q_i = beta * k_j (beta a power of two) for a key j >= 32 that
+    row i sees, so s_ij = beta |k_j|^2 beats the row's first 32 keys by >= 140
+    log2 units: 2^gap overflows fp32 in the first pass, only the exact pass
+    gives a finite, right answer. These rows sit at lanes other than the
+    first of their wave, so a wave-wide check that looked at one lane would
+    miss them.
+  * "mid": the same with a gap of 40 .. 120 log2 units: large but finite
+    exponentials; the first pass is already exact, and the check still sends
+    the workgroup through the second.
+  * "under" (bf16, d 64 / 128): every score of row i far below zero: K's
+    column 0 is raised by 80 for the whole kv head and q_i = -16 e_0, so
+    s·c <= -140 log2 units for every key. A reference taken from outside the
+    row (zero, say) would underflow every exponential; the row's own first
+    keys keep them in range.
+A precondition check computes the gaps (and, for "under", the row's largest
+s·c) in fp64 on the CPU.
+|O_i| stays that of one V row in every case, so the usual tolerances apply.
 """
 import math
 
@@ -63,19 +69,35 @@ def gap_log2(q, k, scale, causal, b, h, i, j, base=None):
 
 
 def make(w, plants, base=None):
-    """plants: (b, h, i, j, beta, kind) with kind "over" or "mid"."""
+    """plants: (b, h, i, j, beta, kind), kind "over", "mid" or "under" (j
+    unused for "under")."""
     q, k, v = make_inputs(w, "cpu")
+    group = q.shape[1] // k.shape[1]
     if w.dtype == torch.float32:
         # the kernel rounds fp32 inputs to bf16 on their way in; with a score
         # of several hundred that rounding alone would move lse by ~0.3, so
         # the planted key rows are made bf16-representable (exact on both
         # sides); every other row keeps its full fp32 value
         k = k.clone()
-        group = q.shape[1] // k.shape[1]
         for b, h, i, j, beta, kind in plants:
             k[b, h // group, j] = k[b, h // group, j].bfloat16().float()
-    q = plant(q.clone(), k, [p[:5] for p in plants])
+    under = [p for p in plants if p[5] == "under"]
+    if under:
+        assert w.dtype == torch.bfloat16 and not w.v_from_k
+        k = k.clone()
+        for b, h, i, j, beta, kind in under:
+            k[b, h // group, :, 0] += 80.0
+    q = plant(q.clone(), k, [p[:5] for p in plants if p[5] != "under"])
+    for b, h, i, j, beta, kind in under:
+        q[b, h, i, :] = 0.0
+        q[b, h, i, 0] = -beta
+    c = w.softmax_scale * LOG2E
     for b, h, i, j, beta, kind in plants:
+        if kind == "under":
+            keys = k[b, h // group, : (i + 1 if w.causal else w.Nkv)].double()
+            top = (keys @ q[b, h, i].double()).max().item() * c
+            assert top <= -140.0 and i % 32 != 0, "row (%d, %d, %d): max s·c %.1f" % (b, h, i, top)
+            continue
         gap = gap_log2(q, k, w.softmax_scale, w.causal, b, h, i, j, base)
         if kind == "over":
             assert gap >= 140.0 and i % 32 != 0, "row (%d, %d, %d): gap %.1f" % (b, h, i, gap)
@@ -131,6 +153,11 @@ MAIN = [
      [(1, 1, 76, 999, 32.0, "over"), (0, 2, 1, 500, 8.0, "mid")]),
     ("d64_fp32_causal", Workload("fb", 1, 2, 1, 190, 190, 64, 64, True, torch.float32, 906),
      [(0, 1, 189, 64, 32.0, "over")]),
+    # every score of the row far below zero (no second pass needed)
+    ("d128_causal_under", Workload("fb", 1, 4, 2, 300, 300, 128, 128, True, torch.bfloat16, 915),
+     [(0, 1, 233, 0, 16.0, "under")]),
+    ("d64_full_under", Workload("fb", 2, 2, 1, 100, 500, 64, 64, False, torch.bfloat16, 916),
+     [(1, 0, 45, 0, 16.0, "under"), (0, 1, 3, 0, 16.0, "under")]),
 ]
 
 
