@@ -95,10 +95,19 @@ __device__ __forceinline__ void store4(float *p, float a, float b, float c, floa
 // spreads the accesses a layout sees across banks, XOR being its own inverse).
 // ---------------------------------------------------------------------------
 
-// Physical chunk of logical chunk c in K row r: XOR with the row, so the 8
-// (or 16) consecutive rows an A-fragment read touches hit distinct banks.
+// Physical chunk of logical chunk c in K row r. LDS has 64 banks of 4 bytes,
+// so 16-byte chunk p of row r lands in bank group (r * D / 8 + p) mod 16, and
+// a ds_read_b128 serves 16 lanes at a time: the 16 rows an A-fragment read
+// touches in one pass must fill the 16 groups. At D = 128 a row is one whole
+// 256-byte bank line and the XOR with r mod 16 does that. At D = 64 two rows
+// share a line (group 8 (r mod 2) + p), so the XOR takes (r / 2) mod 8: rows of
+// one parity then get 8 different chunks (r mod 8 would give rows r and r + 8
+// the same group). Rows r and r + 32 always get the same XOR.
 template <int D>
-__device__ __forceinline__ int k_chunk(int r, int c) { return c ^ (r & (D / 8 - 1)); }
+__device__ __forceinline__ int k_chunk(int r, int c) {
+    constexpr int rows_per_line = (D >= 128) ? 1 : 128 / D;
+    return c ^ ((r / rows_per_line) & (D / 8 - 1));
+}
 
 // Physical chunk of logical chunk c in V row r. A transpose read covers four
 // consecutive rows x 32 bytes per 16 lanes (x 64 bytes per 32 lanes); the XOR
