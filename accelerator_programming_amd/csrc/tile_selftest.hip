@@ -1,7 +1,7 @@
 // Probes of the tile layer, one wave each, for the GPU unit tests: the MFMA
 // fragment layout, the cross-half wave reductions, the swizzled K fragment
 // path of Q·Kᵀ, the transposed V fragment path of P·V, and the lane layout of
-// the LDS transpose read. They
+// the LDS transpose read, and the shader clock under load. They
 // check the primitives the attention kernel is built from, separately from it
 // ("Distilling a 4.5 hour CUDA talk", section 9: unit tests over every
 // load/store/layout/MMA combination).
@@ -113,6 +113,26 @@ __global__ void __launch_bounds__(64) tr16_probe(const int *off, int n, short *o
     for (int e = 0; e < 4; ++e) out[threadIdx.x * 4 + e] = r[e];
 }
 
+// The shader clock a CU runs at while it carries other work: one wave per
+// workgroup reads the shader-cycle counter (s_memtime) and the constant-rate
+// counter (s_memrealtime), sleeps until the latter has advanced by `ticks`
+// (at most `max_iter` sleeps, so every wave ends), reads both again and
+// stores the two differences (cycles, ticks) for its workgroup.
+__global__ void __launch_bounds__(64) clock_probe(uint64_t *out, uint32_t ticks, uint32_t max_iter) {
+    const uint64_t t0 = __builtin_amdgcn_s_memtime();
+    const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+    uint64_t r = r0;
+    for (uint32_t i = 0; i < max_iter && r - r0 < ticks; ++i) {
+        __builtin_amdgcn_s_sleep(2);
+        r = __builtin_amdgcn_s_memrealtime();
+    }
+    const uint64_t t1 = __builtin_amdgcn_s_memtime();
+    if (threadIdx.x == 0) {
+        out[2 * blockIdx.x] = t1 - t0;
+        out[2 * blockIdx.x + 1] = r - r0;
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -162,6 +182,22 @@ int tile_selftest_pv(int d, const void *St, const void *V, void *O, void *stream
 // offsets: 64 device ints; n: number of 16-bit values in LDS (<= 4096).
 // Returns -1 without launching if n is out of range; the caller checks the
 // offsets against n on the host before the call.
+// n_blocks workgroups of the clock probe; out: 2 * n_blocks uint64 (device)
+int tile_selftest_clock(void *out, int n_blocks, unsigned ticks, unsigned max_iter, void *stream) {
+    if (!out || n_blocks < 1 || n_blocks > 65536) return -1;
+    hipLaunchKernelGGL(clock_probe, dim3(n_blocks), dim3(64), 0, (hipStream_t)stream, (uint64_t *)out,
+                       (uint32_t)ticks, (uint32_t)max_iter);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// rate of the counter s_memrealtime reads, in kHz (0 if unknown)
+int tile_selftest_wallclock_khz(void) {
+    int dev = 0, khz = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return 0;
+    return khz;
+}
+
 int tile_selftest_tr16(const void *offsets, int n, void *out, void *stream) {
     if (n < 1 || n > 4096) return -1;
     hipLaunchKernelGGL(tr16_probe, dim3(1), dim3(64), 0, (hipStream_t)stream, (const int *)offsets,

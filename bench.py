@@ -10,14 +10,22 @@ timed region. Prints ONE JSON line.
                 FLOPs 2·B·H_q·N_q·N_kv·(d_qk + d_v), halved when causal
   roofline    = the kernel's own launch time, from HIP events recorded on the
                 stream the kernel is launched on, against the bf16 dense MFMA
-                peak (256 CUs x 4096 flop/clk x 2.4 GHz = 2516.6 TFLOP/s)
-  cpu_baseline= the fp64 oracle timed on the host over a bounded row sample
+                peak (256 CUs x 4096 flop/clk x 2.4 GHz = 2516.6 TFLOP/s):
+                `achieved` from the average launch; the median (the survey's
+                primary figure), min and p90 beside it; the shader clock the
+                chip held under the same load (an in-kernel probe, untimed,
+                after the timed steps) and the fraction of the MFMA rate at
+                that clock
+  cpu_baseline= the fp64 oracle timed on the host over a bounded row sample;
+                `cores` is the threads it used, `host_cores` and
+                `affinity_cores` what the host has and allows
 """
 from __future__ import annotations
 
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -114,7 +122,7 @@ def cpu_baseline(w, q, k, v, target_s: float, threads: int, drop_thr: int = 0):
     return {
         "value": fl / dt / 1e12,
         "unit": "TFLOP/s",
-        "cores": used,
+        **cpu_info(used),
         "kind": "oracle",
         "sample": "%d seeded (b,h,i) rows of %s, each row's unmasked keys only; %.1f s wall, "
                   "%.3g FLOP" % (n, w.name, dt, fl),
@@ -145,7 +153,7 @@ def gemm_cpu_baseline(w, a, b, target_s: float, threads: int):
     return {
         "value": fl / dt / 1e12,
         "unit": "TFLOP/s",
-        "cores": threads,
+        **cpu_info(threads),
         "kind": "oracle",
         "sample": "%d seeded rows of C of %s (fp64 product through numpy's BLAS, %d threads); "
                   "%.1f s wall, %.3g FLOP" % (n, w.name, threads, dt, fl),
@@ -184,6 +192,101 @@ def settle(run, args):
     return warm, steps
 
 
+def clock_probe(run, stream, launch_ms: float, rounds: int = 4):
+    """The shader clock under this load, measured on the GPU: after the timed
+    steps the same launches keep running on `stream` (untimed), in rounds of
+    at least 2 ms of launches (launch_ms each), and beside each round a probe
+    kernel on a second stream (default priority) puts one wave in each of 256
+    workgroups; each wave counts shader cycles (s_memtime) against the
+    constant-rate counter (s_memrealtime) over 1 ms. Returns the median, min
+    and max over all probe waves, or None if the probe library is not
+    built."""
+    import ctypes
+
+    import torch
+    path = os.path.join(ROOT, "accelerator_programming_amd", "libattn_tile_selftest.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.tile_selftest_clock.restype = ctypes.c_int
+    lib.tile_selftest_clock.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_uint,
+                                        ctypes.c_uint, ctypes.c_void_p]
+    lib.tile_selftest_wallclock_khz.restype = ctypes.c_int
+    khz = lib.tile_selftest_wallclock_khz()
+    if khz <= 0:
+        return None
+    n = 256
+    side = torch.cuda.Stream()
+    out = torch.zeros(rounds, 2 * n, dtype=torch.int64, device="cuda")
+    ticks = khz  # 1 ms
+    torch.cuda.synchronize()
+    per_round = max(3, int(math.ceil(2.0 / max(launch_ms, 1e-3))))
+    for r in range(rounds):
+        for _ in range(per_round):
+            run()
+        # the probe starts while this round's launches are still running
+        if lib.tile_selftest_clock(out[r].data_ptr(), n, ticks, 200000, side.cuda_stream) != 0:
+            return None
+        torch.cuda.synchronize()
+    o = out.view(-1, 2).cpu().double()
+    mhz = sorted((o[:, 0] / o[:, 1] * khz / 1e3).tolist())
+    return {"median_mhz": round(mhz[len(mhz) // 2], 1), "min_mhz": round(mhz[0], 1),
+            "max_mhz": round(mhz[-1], 1), "samples": len(mhz),
+            "source": "s_memtime cycles over 1 ms of s_memrealtime in one wave per workgroup "
+                      "of a probe kernel run beside further untimed launches after the timed steps"}
+
+
+def launch_stats(ms):
+    """Per-launch kernel times (HIP events): average, median, min, p90."""
+    xs = sorted(ms)
+    n = len(xs)
+    return {"avg": sum(xs) / n, "median": xs[n // 2], "min": xs[0],
+            "p90": xs[min(n - 1, int(math.ceil(0.9 * n)) - 1)]}
+
+
+def timed_launches(run, steps, stream):
+    """Time exactly `steps` launches of run(): wall clock around all of them
+    (synchronised on both sides) and HIP events around each one, recorded on
+    the stream the kernels are launched on. Then, untimed, the shader clock
+    under the same load (clock_probe). Returns (wall_s, per-launch ms, clock
+    summary)."""
+    import torch
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        run()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return wall, ms, clock_probe(run, stream, sorted(ms)[len(ms) // 2])
+
+
+def kernel_times(ms, clock, work, unit_scale, peak_at_clock=None):
+    """The roofline's timing block: per-launch statistics in ms, the rate at
+    the median launch, and (for MFMA-bound kernels) the fraction of the
+    dense bf16 rate at the sampled clock."""
+    st = launch_stats(ms)
+    out = {"kernel_ms_avg": round(st["avg"], 4), "kernel_ms_median": round(st["median"], 4),
+           "kernel_ms_min": round(st["min"], 4), "kernel_ms_p90": round(st["p90"], 4),
+           "launches": len(ms),
+           "achieved_at_median": round(work / (st["median"] * 1e-3) / unit_scale, 2),
+           "sclk": clock}
+    if peak_at_clock and clock:
+        peak = 256 * 4096 * clock["median_mhz"] * 1e6 / 1e12
+        out["frac_at_sampled_clock"] = round(work / (st["avg"] * 1e-3) / 1e12 / peak, 4)
+    return out
+
+
+def cpu_info(threads_used: int) -> dict:
+    """Host cores: the count the OS reports and the ones this process may use."""
+    return {"cores": threads_used, "host_cores": os.cpu_count(),
+            "affinity_cores": len(os.sched_getaffinity(0))}
+
+
 def gemm_main(args, w) -> int:
     """One step = one C = A·Bᵀ launch over the workload's full shape."""
     import torch
@@ -196,17 +299,9 @@ def gemm_main(args, w) -> int:
     c = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream()
     args.warmup, args.steps = settle(lambda: gemm.gemm_nt(a, b, out=c, stream=stream), args)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        gemm.gemm_nt(a, b, out=c, stream=stream)
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern_avg_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / args.steps
+    wall, kern_ms, clock = timed_launches(lambda: gemm.gemm_nt(a, b, out=c, stream=stream),
+                                          args.steps, stream)
+    kern_avg_ms = sum(kern_ms) / len(kern_ms)
     ms_per_step = wall * 1e3 / args.steps
     flops = w.flops()
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -238,7 +333,7 @@ def gemm_main(args, w) -> int:
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_for_current_kernel(w.name, "tile_gemm_" + args.config,
                                                            gemm_source_sha()),
-                     "kernel_ms_avg": round(kern_avg_ms, 4),
+                     **kernel_times(kern_ms, clock, flops, 1e12, peak_at_clock=True),
                      "kernel": "attn::gemm_bf16_nt_kernel"},
         "cpu_baseline": cpu,
     }
@@ -261,16 +356,9 @@ def rope_main(args) -> int:
     base = args.rope or 500000.0
     stream = torch.cuda.current_stream()
     args.warmup, args.steps = settle(lambda: attn.attn_rope_bf16(q, y, base, stream), args)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        attn.attn_rope_bf16(q, y, base, stream)
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / args.steps
+    wall, kern_list, clock = timed_launches(lambda: attn.attn_rope_bf16(q, y, base, stream),
+                                            args.steps, stream)
+    kern_ms = sum(kern_list) / len(kern_list)
     nbytes = 2 * q.numel() * q.element_size()
     gbs = nbytes / (kern_ms * 1e-3) / 1e9
     line = {
@@ -292,7 +380,8 @@ def rope_main(args) -> int:
                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                      "traffic": traffic_for_current_kernel("R1_rope_B1_H32_N16384_d128",
                                                            "attn_rope_R1"),
-                     "kernel_ms_avg": round(kern_ms, 4), "kernel": "attn::rope_bf16_kernel"},
+                     **kernel_times(kern_list, clock, nbytes, 1e9),
+                     "kernel": "attn::rope_bf16_kernel"},
         "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
@@ -381,19 +470,9 @@ def main() -> int:
     stream = torch.cuda.current_stream()
     args.warmup, args.steps = settle(lambda: op.run(q, k, v, o, lse, stream=stream), args)
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        op.run(q, k, v, o, lse, stream=stream)
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall, kern_ms, clock = timed_launches(lambda: op.run(q, k, v, o, lse, stream=stream),
+                                          args.steps, stream)
     op.close()
-
-    kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     kern_avg_ms = sum(kern_ms) / len(kern_ms)
     ms_per_step = wall * 1e3 / args.steps
     flops = w.flops()
@@ -433,14 +512,14 @@ def main() -> int:
                       "traffic": traffic_for_current_kernel(
                           w.name, "attn_fwd_" + args.config + ("_dropout" if drop_thr else "")
                           + ("_rope" if args.rope else "")),
-                      "kernel_ms_avg": round(kern_avg_ms, 4),
+                      **kernel_times(kern_ms, clock, flops, 1e12, peak_at_clock=True),
                       "kernel": ("attn::rope_bf16_kernel (K) + " if args.rope else "")
                       + kernel_name(w, drop_thr > 0, args.rope > 0)} if not w.decode else
                      {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                       "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                       "traffic": traffic_for_current_kernel(w.name, "attn_split_" + args.config,
                                                                   kernel_source_sha(split=True)),
-                      "kernel_ms_avg": round(kern_avg_ms, 4),
+                      **kernel_times(kern_ms, clock, w.io_bytes(), 1e9),
                       "tflops": round(achieved, 2),
                       "kernel": kernel_name(w)}),
         "cpu_baseline": cpu,
