@@ -52,45 +52,51 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError("HIP library %s is not built; run "
                                "`python -m accelerator_programming_amd.build`" % LIB_PATH)
-        L = ctypes.CDLL(LIB_PATH)
-        P = ctypes.c_void_p
-        I64 = ctypes.c_int64
-        L.attn_fwd_create.restype = ctypes.c_int
-        L.attn_fwd_create.argtypes = [ctypes.POINTER(P), I64, I64, I64, I64, I64, ctypes.c_int32,
-                                      ctypes.c_float]
-        L.attn_fwd_create_ex.restype = ctypes.c_int
-        L.attn_fwd_create_ex.argtypes = [ctypes.POINTER(AttnFwdParams), ctypes.POINTER(P)]
-        L.attn_fwd_run.restype = ctypes.c_int
-        L.attn_fwd_run.argtypes = [P, P, P, P, P, P, P]
-        L.attn_fwd_destroy.restype = None
-        L.attn_fwd_destroy.argtypes = [P]
-        L.attn_status_str.restype = ctypes.c_char_p
-        L.attn_status_str.argtypes = [ctypes.c_int]
-        L.attn_fwd_split_count.restype = ctypes.c_int32
-        L.attn_fwd_split_count.argtypes = [P]
-        L.attn_fwd_split_workspace_bytes.restype = I64
-        L.attn_fwd_split_workspace_bytes.argtypes = [P, ctypes.c_int32]
-        L.attn_fwd_run_split.restype = ctypes.c_int
-        L.attn_fwd_run_split.argtypes = [P, P, P, P, P, P, ctypes.c_int32, P, I64, P]
-        L.attn_fwd_run_split_noalloc.restype = ctypes.c_int
-        L.attn_fwd_run_split_noalloc.argtypes = [P, P, P, P, P, P, ctypes.c_int32, P]
-        L.attn_fwd_plan_info.restype = ctypes.c_int
-        L.attn_fwd_plan_info.argtypes = [P, ctypes.POINTER(I64), ctypes.POINTER(ctypes.c_int32),
-                                         ctypes.POINTER(ctypes.c_int32),
-                                         ctypes.POINTER(ctypes.c_int32),
-                                         ctypes.POINTER(ctypes.c_int32)]
-        L.attn_fwd_run_dropout.restype = ctypes.c_int
-        L.attn_fwd_run_dropout.argtypes = [P, P, P, P, P, P, ctypes.c_float, ctypes.c_uint64, P]
-        L.attn_rope_bf16.restype = ctypes.c_int
-        L.attn_rope_bf16.argtypes = [P, P, I64, I64, I64, I64, P, P, ctypes.c_float, P]
-        L.attn_fwd_rope_workspace_bytes.restype = I64
-        L.attn_fwd_rope_workspace_bytes.argtypes = [P]
-        L.attn_fwd_run_rope.restype = ctypes.c_int
-        L.attn_fwd_run_rope.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, I64, P]
-        L.tile_gemm_bf16_nt.restype = ctypes.c_int
-        L.tile_gemm_bf16_nt.argtypes = [I64, I64, I64, P, I64, P, I64, P, I64, P]
-        _lib = L
+        _lib = bind(LIB_PATH)
     return _lib
+
+
+def bind(path: str) -> ctypes.CDLL:
+    """Load a build of the library at `path` with the C prototypes set (the
+    tests also load the timing-perturbation build this way)."""
+    L = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    L.attn_fwd_create.restype = ctypes.c_int
+    L.attn_fwd_create.argtypes = [ctypes.POINTER(P), I64, I64, I64, I64, I64, ctypes.c_int32,
+                                  ctypes.c_float]
+    L.attn_fwd_create_ex.restype = ctypes.c_int
+    L.attn_fwd_create_ex.argtypes = [ctypes.POINTER(AttnFwdParams), ctypes.POINTER(P)]
+    L.attn_fwd_run.restype = ctypes.c_int
+    L.attn_fwd_run.argtypes = [P, P, P, P, P, P, P]
+    L.attn_fwd_destroy.restype = None
+    L.attn_fwd_destroy.argtypes = [P]
+    L.attn_status_str.restype = ctypes.c_char_p
+    L.attn_status_str.argtypes = [ctypes.c_int]
+    L.attn_fwd_split_count.restype = ctypes.c_int32
+    L.attn_fwd_split_count.argtypes = [P]
+    L.attn_fwd_split_workspace_bytes.restype = I64
+    L.attn_fwd_split_workspace_bytes.argtypes = [P, ctypes.c_int32]
+    L.attn_fwd_run_split.restype = ctypes.c_int
+    L.attn_fwd_run_split.argtypes = [P, P, P, P, P, P, ctypes.c_int32, P, I64, P]
+    L.attn_fwd_run_split_noalloc.restype = ctypes.c_int
+    L.attn_fwd_run_split_noalloc.argtypes = [P, P, P, P, P, P, ctypes.c_int32, P]
+    L.attn_fwd_plan_info.restype = ctypes.c_int
+    L.attn_fwd_plan_info.argtypes = [P, ctypes.POINTER(I64), ctypes.POINTER(ctypes.c_int32),
+                                     ctypes.POINTER(ctypes.c_int32),
+                                     ctypes.POINTER(ctypes.c_int32),
+                                     ctypes.POINTER(ctypes.c_int32)]
+    L.attn_fwd_run_dropout.restype = ctypes.c_int
+    L.attn_fwd_run_dropout.argtypes = [P, P, P, P, P, P, ctypes.c_float, ctypes.c_uint64, P]
+    L.attn_rope_bf16.restype = ctypes.c_int
+    L.attn_rope_bf16.argtypes = [P, P, I64, I64, I64, I64, P, P, ctypes.c_float, P]
+    L.attn_fwd_rope_workspace_bytes.restype = I64
+    L.attn_fwd_rope_workspace_bytes.argtypes = [P]
+    L.attn_fwd_run_rope.restype = ctypes.c_int
+    L.attn_fwd_run_rope.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, I64, P]
+    L.tile_gemm_bf16_nt.restype = ctypes.c_int
+    L.tile_gemm_bf16_nt.argtypes = [I64, I64, I64, P, I64, P, I64, P, I64, P]
+    return L
 
 
 def attn_status_str(status: int) -> str:

@@ -163,7 +163,7 @@ attn_fwd_kernel(const KernelArgs a) {
     int b, h, qt;
     {
         const int n_groups = a.B * a.Hkv;
-        const int bid = blockIdx.x;
+        const int bid = work_index(blockIdx.x, gridDim.x);
         if (n_groups % 8 == 0) {
             const int xcd = bid % 8, idx = bid / 8;
             const int per_round = (n_groups / 8) * a.group;  // WGs of one q-tile on one XCD
@@ -269,6 +269,7 @@ attn_fwd_kernel(const KernelArgs a) {
         m0 += (is_v ? NS * C::TILE * 2 : 0) + stage_off + (uint32_t)(4 * u) * 1024u;
         // M0 (the LDS destination) is written inside the statement, and the
         // DMA is followed by a wait state (see dma16_buf_to_lds)
+        perturb_pause();
         asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds\n\ts_nop 0"
                      :
                      : "s"(m0), "v"(is_v ? voff_v[u] : voff_k[u]), "s"(rsrc)

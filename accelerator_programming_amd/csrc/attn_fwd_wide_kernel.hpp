@@ -68,8 +68,9 @@ attn_fwd_wide_kernel(const KernelArgs a) {
 
     // ---- work item ----------------------------------------------------------
     const int BH = a.B * a.Hq;
-    const int bh = blockIdx.x % BH;
-    int qt = blockIdx.x / BH;
+    const uint32_t wid = work_index(blockIdx.x, gridDim.x);
+    const int bh = wid % BH;
+    int qt = wid / BH;
     if (CAUSAL) qt = a.n_qtiles - 1 - qt;
     const int b = bh / a.Hq, h = bh % a.Hq, hk = h / a.group;
     const __bf16 *__restrict__ Qp = (const __bf16 *)a.q + b * a.q_sb + h * a.q_sh;
@@ -119,6 +120,7 @@ attn_fwd_wide_kernel(const KernelArgs a) {
         const u32x4 rv = buffer_rsrc(Vp + (int64_t)T * TK * a.v_sn,
                                      (uint32_t)(((int64_t)(rem - 1) * a.v_sn + DV) * 2));
         unsigned char *st = lds + stage * C::STAGE_B;
+        perturb_pause();
 #pragma unroll
         for (int u = 0; u < C::KWIN_W; ++u) dma16_buf_to_lds(rk, koff[u], st + (C::NWAVE * u + w) * 1024);
 #pragma unroll

@@ -81,8 +81,9 @@ attn_split_kernel(const SplitArgs sa) {
 
     // ---- work item: blockIdx = (split, batch, kv head), kv head fastest ----
     const int n_groups = a.B * a.Hkv;
-    const int split = blockIdx.x / n_groups;
-    const int b = (blockIdx.x % n_groups) / a.Hkv, hk = (blockIdx.x % n_groups) % a.Hkv;
+    const uint32_t wid = work_index(blockIdx.x, gridDim.x);
+    const int split = wid / n_groups;
+    const int b = (wid % n_groups) / a.Hkv, hk = (wid % n_groups) % a.Hkv;
     const int k_begin = split * sa.split_len;
     const int k_end = min(a.Nkv, k_begin + sa.split_len);
     const int n_tiles = k_end > k_begin ? (k_end - k_begin + TK - 1) / TK : 0;
@@ -116,12 +117,13 @@ attn_split_kernel(const SplitArgs sa) {
     // ranges lie at equal power-of-two strides, do not all read the same
     // offsets of their ranges at the same time (measured: +11 % bandwidth
     // on 512 workgroups of 32 tiles). The softmax takes the keys in any order.
-    const int rot = n_tiles > 0 ? (int)(blockIdx.x % (uint32_t)n_tiles) : 0;
+    const int rot = n_tiles > 0 ? (int)(wid % (uint32_t)n_tiles) : 0;
     auto phys = [&](int T) { const int t = T + rot; return t >= n_tiles ? t - n_tiles : t; };
     const int dma_r = lane / C::CPR, dma_p = lane % C::CPR;
     auto copy_tile = [&](int T, int stage) __attribute__((always_inline)) {
         if (T >= n_tiles || (T & 3) != w) return;
         unsigned char *st = lds + stage * C::STAGE_B;
+        perturb_pause();
         const int key0 = k_begin + phys(T) * TK;
         const int rem = k_end - key0;  // >= 1
 #pragma unroll
@@ -282,7 +284,7 @@ __global__ void __launch_bounds__(256) attn_split_merge(const float *__restrict_
     __shared__ f32x4 red[SLOTS][CG];
     const int t = threadIdx.x;
     const int c = t % CG, j = t / CG;
-    const int64_t row = blockIdx.x;
+    const int64_t row = work_index(blockIdx.x, gridDim.x);
     f32x4 v[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {

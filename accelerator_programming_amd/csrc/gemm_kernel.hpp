@@ -95,7 +95,7 @@ gemm_bf16_nt_kernel(const GemmArgs a) {
     int tm, tn;
     {
         const int T = a.tiles_m * a.tiles_n;
-        const int bid = blockIdx.x;
+        const int bid = work_index(blockIdx.x, gridDim.x);
         int t = bid;
         if (T % 8 == 0) t = (bid % 8) * (T / 8) + bid / 8;
         constexpr int GM = 8;
@@ -150,6 +150,7 @@ gemm_bf16_nt_kernel(const GemmArgs a) {
         m0v = __builtin_amdgcn_readfirstlane(m0v + (uint32_t)win * 1024u);
         // M0 (the LDS destination) is written inside the statement, and the
         // DMA is followed by a wait state (see dma16_buf_to_lds in tile.hpp)
+        perturb_pause();
         asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds\n\ts_nop 0"
                      :
                      : "s"(m0v), "v"(off), "s"(rsrc)

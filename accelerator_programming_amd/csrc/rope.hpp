@@ -82,8 +82,9 @@ __global__ void __launch_bounds__(256) rope_bf16_kernel(const RopeArgs a) {
     const int slots = 256 / cpr;
     const int c = threadIdx.x % cpr, slot = threadIdx.x / cpr;
     if (slot >= slots) return;
-    const int rb = blockIdx.x % a.row_blocks;
-    const int64_t bh = blockIdx.x / a.row_blocks;
+    const uint32_t wid = work_index(blockIdx.x, gridDim.x);
+    const int rb = wid % a.row_blocks;
+    const int64_t bh = wid / a.row_blocks;
     const int64_t h = bh % a.H, b = bh / a.H;
     double f[4];
 #pragma unroll

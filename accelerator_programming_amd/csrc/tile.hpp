@@ -189,6 +189,40 @@ __device__ __forceinline__ bf16x8 vt_frag_at(uint32_t p, int kc) {
     return __builtin_bit_cast(bf16x8, v8);
 }
 
+// ---------------------------------------------------------------------------
+// Timing perturbation, for test builds only. A library compiled with
+// -DATTN_PERTURB=<seed> runs every kernel with its workgroups taking their
+// work items in a seeded permuted order and with a pseudo-random pause of up
+// to 7 s_sleeps before every LDS-DMA of the main kernel and the GEMM, and
+// before every tile copy (a burst of DMAs) of the wide-head and split-KV
+// kernels (one pause per DMA there raised the V-in-K kernel above its
+// register budget). Arithmetic and data placement are
+// unchanged, so such a build must reproduce the normal build's outputs bit
+// for bit; it exists so that the parity tests also run with the copies,
+// waits and barriers pulled out of their usual timing.
+// ---------------------------------------------------------------------------
+#ifdef ATTN_PERTURB
+// work item of workgroup bid: (bid * p + seed) mod grid with p a prime above
+// 2^32, so a bijection of [0, grid) for every grid size
+__device__ __forceinline__ uint32_t work_index(uint32_t bid, uint32_t grid) {
+    return (uint32_t)(((uint64_t)bid * 4294967311ull + (uint64_t)(ATTN_PERTURB)) % (uint64_t)grid);
+}
+__device__ __forceinline__ void perturb_pause() {
+    uint32_t h = __builtin_amdgcn_readfirstlane(blockIdx.x * 0x9E3779B9u ^ (threadIdx.x >> 6) * 0x85EBCA6Bu) ^
+                 (uint32_t)__builtin_amdgcn_s_memtime();
+    h ^= h >> 16;
+    h *= 0x7FEB352Du;
+    h ^= h >> 15;
+    h *= 0x846CA68Bu;
+    h ^= h >> 16;
+    const uint32_t n = __builtin_amdgcn_readfirstlane(h & 7u);
+    for (uint32_t i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(2);
+}
+#else
+__device__ __forceinline__ uint32_t work_index(uint32_t bid, uint32_t) { return bid; }
+__device__ __forceinline__ void perturb_pause() {}
+#endif
+
 // LDS-DMA: 16 bytes from gptr (per lane) into LDS at lds_base + 16 * lane,
 // lds_base wave-uniform (it goes through M0). Issued as inline assembly so
 // that the compiler does not treat it as a store that every later LDS read
