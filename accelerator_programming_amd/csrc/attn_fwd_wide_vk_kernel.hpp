@@ -89,10 +89,12 @@ __device__ __forceinline__ int wide_vk_chunk(int r, int c) {
 // different LDS read instructions is not relied on), then issues read ks + 6
 // into slot ks % 6 right after the MFMA of step ks (which took its operand
 // at issue) and waits for read ks (ks >= 1) with lgkmcnt(min(5, 17 - ks)),
-// counting only its own ds_read_b128s, which complete in order. The block
-// ends with enough wait states for VALU, LDS or memory reads of the
-// accumulator (the compiler does not see the MFMA latency through an asm
-// statement).
+// counting only its own ds_read_b128s, which complete in order. Even
+// k-steps accumulate into s and odd ones into t, two independent chains
+// instead of one chain of 18 dependent MFMAs (C5 +1.4 %); the block returns
+// s + t. It ends with enough wait states for VALU, LDS or memory reads of
+// the accumulators (the compiler does not see the MFMA latency through an
+// asm statement).
 #define WIDE_VK_CLOBBERS                                                                              \
     "v176", "v177", "v178", "v179", "v180", "v181", "v182", "v183", "v184", "v185", "v186", "v187", \
         "v188", "v189", "v190", "v191", "v192", "v193", "v194", "v195", "v196", "v197", "v198", "v199"
@@ -117,23 +119,23 @@ __device__ __forceinline__ int wide_vk_chunk(int r, int c) {
 #define WIDE_VK_KR17 "ds_read_b128 v[196:199], %[kb1] offset:1024\n\t"
 // MFMA of step ks after waiting for its read; C: the accumulator input
 #define WIDE_VK_MM0 "s_waitcnt lgkmcnt(0)\n\tv_mfma_f32_16x16x32_bf16 %[s], v[176:179], %[q0], " "0" "\n\t"
-#define WIDE_VK_MM1 "s_waitcnt lgkmcnt(5)\n\tv_mfma_f32_16x16x32_bf16 %[s], v[180:183], %[q1], " "%[s]" "\n\t"
+#define WIDE_VK_MM1 "s_waitcnt lgkmcnt(5)\n\tv_mfma_f32_16x16x32_bf16 %[t], v[180:183], %[q1], " "0" "\n\t"
 #define WIDE_VK_MM2 "s_waitcnt lgkmcnt(5)\n\tv_mfma_f32_16x16x32_bf16 %[s], v[184:187], %[q2], " "%[s]" "\n\t"
-#define WIDE_VK_MM3 "s_waitcnt lgkmcnt(5)\n\tv_mfma_f32_16x16x32_bf16 %[s], v[188:191], %[q3], " "%[s]" "\n\t"
+#define WIDE_VK_MM3 "s_waitcnt lgkmcnt(5)\n\tv_mfma_f32_16x16x32_bf16 %[t], v[188:191], %[q3], " "%[t]" "\n\t"
 #define WIDE_VK_MM4 "s_waitcnt lgkmcnt(5)\n\tv_mfma_f32_16x16x32_bf16 %[s], v[192:195], %[q4], " "%[s]" "\n\t"
-#define WIDE_VK_MM5 "s_waitcnt lgkmcnt(5)\n\tv_mfma_f32_16x16x32_bf16 %[s], v[196:199], %[q5], " "%[s]" "\n\t"
+#define WIDE_VK_MM5 "s_waitcnt lgkmcnt(5)\n\tv_mfma_f32_16x16x32_bf16 %[t], v[196:199], %[q5], " "%[t]" "\n\t"
 #define WIDE_VK_MM6 "s_waitcnt lgkmcnt(5)\n\tv_mfma_f32_16x16x32_bf16 %[s], v[176:179], %[q6], " "%[s]" "\n\t"
-#define WIDE_VK_MM7 "s_waitcnt lgkmcnt(5)\n\tv_mfma_f32_16x16x32_bf16 %[s], v[180:183], %[q7], " "%[s]" "\n\t"
+#define WIDE_VK_MM7 "s_waitcnt lgkmcnt(5)\n\tv_mfma_f32_16x16x32_bf16 %[t], v[180:183], %[q7], " "%[t]" "\n\t"
 #define WIDE_VK_MM8 "s_waitcnt lgkmcnt(5)\n\tv_mfma_f32_16x16x32_bf16 %[s], v[184:187], %[q8], " "%[s]" "\n\t"
-#define WIDE_VK_MM9 "s_waitcnt lgkmcnt(5)\n\tv_mfma_f32_16x16x32_bf16 %[s], v[188:191], %[q9], " "%[s]" "\n\t"
+#define WIDE_VK_MM9 "s_waitcnt lgkmcnt(5)\n\tv_mfma_f32_16x16x32_bf16 %[t], v[188:191], %[q9], " "%[t]" "\n\t"
 #define WIDE_VK_MM10 "s_waitcnt lgkmcnt(5)\n\tv_mfma_f32_16x16x32_bf16 %[s], v[192:195], %[q10], " "%[s]" "\n\t"
-#define WIDE_VK_MM11 "s_waitcnt lgkmcnt(5)\n\tv_mfma_f32_16x16x32_bf16 %[s], v[196:199], %[q11], " "%[s]" "\n\t"
+#define WIDE_VK_MM11 "s_waitcnt lgkmcnt(5)\n\tv_mfma_f32_16x16x32_bf16 %[t], v[196:199], %[q11], " "%[t]" "\n\t"
 #define WIDE_VK_MM12 "s_waitcnt lgkmcnt(5)\n\tv_mfma_f32_16x16x32_bf16 %[s], v[176:179], %[q12], " "%[s]" "\n\t"
-#define WIDE_VK_MM13 "s_waitcnt lgkmcnt(4)\n\tv_mfma_f32_16x16x32_bf16 %[s], v[180:183], %[q13], " "%[s]" "\n\t"
+#define WIDE_VK_MM13 "s_waitcnt lgkmcnt(4)\n\tv_mfma_f32_16x16x32_bf16 %[t], v[180:183], %[q13], " "%[t]" "\n\t"
 #define WIDE_VK_MM14 "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_16x16x32_bf16 %[s], v[184:187], %[q14], " "%[s]" "\n\t"
-#define WIDE_VK_MM15 "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_16x16x32_bf16 %[s], v[188:191], %[q15], " "%[s]" "\n\t"
+#define WIDE_VK_MM15 "s_waitcnt lgkmcnt(2)\n\tv_mfma_f32_16x16x32_bf16 %[t], v[188:191], %[q15], " "%[t]" "\n\t"
 #define WIDE_VK_MM16 "s_waitcnt lgkmcnt(1)\n\tv_mfma_f32_16x16x32_bf16 %[s], v[192:195], %[q16], " "%[s]" "\n\t"
-#define WIDE_VK_MM17 "s_waitcnt lgkmcnt(0)\n\tv_mfma_f32_16x16x32_bf16 %[s], v[196:199], %[q17], " "%[s]" "\n\t"
+#define WIDE_VK_MM17 "s_waitcnt lgkmcnt(0)\n\tv_mfma_f32_16x16x32_bf16 %[t], v[196:199], %[q17], " "%[t]" "\n\t"
 
 __device__ __forceinline__ void wide_vk_kreads0(uint32_t kb0, uint32_t kb1) {
     asm volatile(WIDE_VK_KR0 WIDE_VK_KR1 WIDE_VK_KR2 WIDE_VK_KR3 WIDE_VK_KR4 WIDE_VK_KR5
@@ -143,21 +145,21 @@ __device__ __forceinline__ void wide_vk_kreads0(uint32_t kb0, uint32_t kb1) {
 }
 
 __device__ __forceinline__ f32x4 wide_vk_qk(const bf16x8 (&q)[18], uint32_t kb0, uint32_t kb1) {
-    f32x4 s;
+    f32x4 s, t;
     asm volatile(WIDE_VK_MM0 WIDE_VK_KR6 WIDE_VK_MM1 WIDE_VK_KR7 WIDE_VK_MM2 WIDE_VK_KR8
                  WIDE_VK_MM3 WIDE_VK_KR9 WIDE_VK_MM4 WIDE_VK_KR10 WIDE_VK_MM5 WIDE_VK_KR11
                  WIDE_VK_MM6 WIDE_VK_KR12 WIDE_VK_MM7 WIDE_VK_KR13 WIDE_VK_MM8 WIDE_VK_KR14
                  WIDE_VK_MM9 WIDE_VK_KR15 WIDE_VK_MM10 WIDE_VK_KR16 WIDE_VK_MM11 WIDE_VK_KR17
                  WIDE_VK_MM12 WIDE_VK_MM13 WIDE_VK_MM14 WIDE_VK_MM15 WIDE_VK_MM16 WIDE_VK_MM17
                  "s_nop 7\n\ts_nop 7\n\ts_nop 3"
-                 : [s] "=&a"(s)
+                 : [s] "=&a"(s), [t] "=&a"(t)
                  : [kb0] "v"(kb0), [kb1] "v"(kb1),
                    [q0] "v"(q[0]), [q1] "v"(q[1]), [q2] "v"(q[2]), [q3] "v"(q[3]), [q4] "v"(q[4]),
                    [q5] "v"(q[5]), [q6] "v"(q[6]), [q7] "v"(q[7]), [q8] "v"(q[8]), [q9] "v"(q[9]),
                    [q10] "v"(q[10]), [q11] "v"(q[11]), [q12] "v"(q[12]), [q13] "v"(q[13]),
                    [q14] "v"(q[14]), [q15] "v"(q[15]), [q16] "v"(q[16]), [q17] "v"(q[17])
                  : WIDE_VK_CLOBBERS, "memory");
-    return s;
+    return s + t;
 }
 
 template <int DQK, int DV, bool CAUSAL>
