@@ -7,30 +7,33 @@
 // carried by a per-row reference and normalizer, section 7). What differs is
 // how the 8 waves of a workgroup (two per SIMD) share the work of one 32-row
 // query tile and a 32-key tile:
-//  * Scores: waves 0..3, w = 2 rh + kh, each own the 16 x 16 block of keys
+//  * Score waves 0..3, w = 2 rh + kh, each own the 16 x 16 block of keys
 //    16 kh .. 16 kh + 15 and rows 16 rh .. 16 rh + 15 and compute it whole
 //    (Sᵀ = K·Qᵀ, 18 k-steps of v_mfma_f32_16x16x32_bf16, their 16 rows of Q
 //    held in registers), apply the mask and the exponential to it and write
 //    P (bf16) to LDS.
-//  * Copies: waves 4..7 move the K tiles into LDS (LDS-DMA).
-//  * Values: after one barrier every wave reads all of P and accumulates
-//    output columns 64 w .. 64 w + 63 for all 32 rows (O = P·V split over
-//    the value columns), reading its Vᵀ fragments from the K tile.
-//  Each SIMD holds one score wave and one copy wave, so its MFMA work per
-//  tile is 18 16x16 + 8 32x32 MFMAs either way; no MFMA or exponential is
-//  repeated; the only per-tile exchange is the 2 KB of P. Two waves per SIMD
-//  keep more LDS requests in flight than one, and one wave's MFMAs run while
-//  the other waits.
+//  * Value waves 4..7 (vw = w - 4) move the K tiles into LDS (LDS-DMA) and,
+//    after the barrier that publishes a tile's P, read all of it and
+//    accumulate output columns 128 vw .. 128 vw + 127 for all 32 rows
+//    (O = P·V split over the value columns), reading their Vᵀ fragments from
+//    the K tile.
+//  Each SIMD holds one score wave and one value wave: in each tile period
+//  the score wave's MFMAs for tile T + 1 and the value wave's for tile T
+//  share the SIMD's matrix pipe (18 16x16 + 8 32x32 MFMAs), and each wave's
+//  LDS waits, exponentials and copies run beside the other's MFMAs. No MFMA
+//  or exponential is repeated; the only per-tile exchange is the 2 KB of P.
+//  The two roles run separate code, so that each keeps only its own
+//  registers live (the Q fragments, or the O accumulators).
 //  * Row statistics: the reference m of a row (the maximum over the first 32
 //    keys) and, at the end, its normalizer l are the two key halves' values
 //    combined through LDS.
 //  * K tiles (32 keys x 1152 bytes) sit in a four-stage LDS ring: after tile
-//    T's barrier one pair of copy waves issues tile T + 3 (the pairs take
+//    T's barrier one pair of value waves issues tile T + 3 (the pairs take
 //    turns), and the barrier two tiles later waits for it.
 //  * Software pipeline, one barrier per tile: after the barrier that
-//    publishes P of tile T, a wave issues the LDS reads of P·V(T) and (score
-//    waves) the first K fragment reads of tile T + 1's scores, then the score
-//    MFMAs of T + 1, then the P·V MFMAs of T, then P of T + 1 and the barrier.
+//    publishes P of tile T, the score waves read K of tile T + 1, run its
+//    score MFMAs and write its P; the value waves read P and Vᵀ of tile T,
+//    issue the copy of tile T + 3 and run the P·V MFMAs of T.
 //  * K rows are 72 16-byte chunks. Chunk c of row r is stored at
 //    c ^ s(r), s(r) = t ^ 4 (t & 1), t = (r / 2) % 8; with the k-group
 //    order below the 16 lanes served together by a fragment read
@@ -63,12 +66,12 @@ struct WideVkCfg {
     static constexpr int SOFF = POFF + 2 * PBUF_B; // row statistics: [2 key halves][32 rows] + m[32]
     static constexpr int LDS_BYTES = SOFF + 3 * TQ * 4;
     static constexpr int KWIN_W = KTILE_B / 1024 / 2;  // 1 KB copies per copy wave per copied tile
-    static constexpr int CBW = DV / 32 / NWAVE;                    // 32-column blocks of O per wave
+    static constexpr int CBW = DV / 32 / (NWAVE - NSW);            // 32-column blocks of O per value wave
     static_assert(NWAVE - NSW == 4, "two pairs of copy waves");
     static_assert(KTILE_B % 2048 == 0, "tile pieces must split over a pair of copy waves");
     static_assert(NKS == 18, "the score block is written for 18 k-steps");
     static_assert(KCH % 8 == 0, "the swizzle permutes aligned groups of 8 chunks");
-    static_assert(CBW == 2 && DV <= DQK, "value columns 64w .. 64w + 63");
+    static_assert(CBW == 4 && DV <= DQK, "value columns 128 vw .. 128 vw + 127");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
@@ -152,7 +155,7 @@ __device__ __forceinline__ f32x4 wide_vk_qk(const bf16x8 (&q)[18], uint32_t kb0,
                  WIDE_VK_MM9 WIDE_VK_KR15 WIDE_VK_MM10 WIDE_VK_KR16 WIDE_VK_MM11 WIDE_VK_KR17
                  WIDE_VK_MM12 WIDE_VK_MM13 WIDE_VK_MM14 WIDE_VK_MM15 WIDE_VK_MM16 WIDE_VK_MM17
                  "s_nop 7\n\ts_nop 7\n\ts_nop 3"
-                 : [s] "=&a"(s), [t] "=&a"(t)
+                 : [s] "=&v"(s), [t] "=&v"(t)
                  : [kb0] "v"(kb0), [kb1] "v"(kb1),
                    [q0] "v"(q[0]), [q1] "v"(q[1]), [q2] "v"(q[2]), [q3] "v"(q[3]), [q4] "v"(q[4]),
                    [q5] "v"(q[5]), [q6] "v"(q[6]), [q7] "v"(q[7]), [q8] "v"(q[8]), [q9] "v"(q[9]),
@@ -174,10 +177,11 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const bool sw = w < C::NSW;                  // a score wave (else a copy wave)
+    const bool sw = w < C::NSW;                  // a score wave (else a value wave)
     const int l32 = lane & 31, g = lane >> 5;    // 32x32 fragments (P·V)
     const int l16 = lane & 15, G = lane >> 4;    // 16x16 fragments (scores)
     const int kh = w & 1, rh = (w >> 1) & 1;     // a score wave's block
+    const int vw = (w - C::NSW) & 3;             // a value wave's index
     // k-group of this lane's 8 contraction elements in a k-step: quarter G
     // takes group 0, 3, 1, 2 for G = 0..3. With the row swizzle this order
     // makes every K fragment read free of LDS bank conflicts (measured with
@@ -204,36 +208,35 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
     // tiles from this index on need the causal or key-range mask
     const int first_masked = CAUSAL ? min(q0 / TK, a.Nkv / TK) : a.Nkv / TK;
 
-    // ---- Q of the block's 16 rows (B operands, score waves), resident -------
-    bf16x8 qf[C::NKS];
-#pragma unroll
-    for (int ks = 0; ks < C::NKS; ++ks) {
-        u32x4 v = {0, 0, 0, 0};
-        if (sw && srow < a.Nq) v = load8_bf16(Qp + (int64_t)srow * a.q_sn + 32 * ks + 8 * kg);
-        qf[ks] = u32x4_as_bf16x8(v);
-    }
+    // this wave's LDS accesses are done, then every wave reaches this point
+    // (also a compiler memory barrier)
+    auto lds_barrier = [&]() __attribute__((always_inline)) {
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    };
+    float *stat = (float *)(lds + C::SOFF);  // [kh][32] per-half row values, then m[32]
 
-    // ---- K copies: copy waves 4, 5 copy the even tiles, 6, 7 the odd ones,
-    // so that a pair's copies of a tile are its only ones in flight when it
-    // waits for them (vmcnt(0)) two tiles later. Piece u of pair member m is
-    // the 1 KB at (2u + m) KB of the tile; lane i moves its 16-byte unit
-    // 64 (2u + m) + i, which holds the logical chunk the swizzle puts there.
-    // The byte offsets inside a tile are the same for every tile; the copies
-    // go through a buffer resource that ends at the last key, so rows past it
-    // read as zeros (finite, masked). -------------------------------------
-    const int cpair = ((w - C::NSW) >> 1) & 1, cm = (w - C::NSW) & 1;
-    uint32_t koff[C::KWIN_W];
+    // ---- K copies (value waves): waves 4, 5 copy the even tiles, 6, 7 the
+    // odd ones, so that a pair's copies of a tile are its only ones in flight
+    // when it waits for them (vmcnt(0)) two tiles later. Piece u of pair
+    // member cm is the 1 KB at (2u + cm) KB of the tile; lane i moves its
+    // 16-byte unit 64 (2u + cm) + i, which holds the logical chunk the
+    // swizzle puts there. The byte offsets inside a tile are the same for
+    // every tile; the copies go through a buffer resource that ends at the
+    // last key, so rows past it read as zeros (finite, masked). ----------
+    const int cpair = vw >> 1, cm = vw & 1;
+    auto copy_offsets = [&](uint32_t (&koff)[C::KWIN_W]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < C::KWIN_W; ++u) {
-        const int p = (2 * u + cm) * 64 + lane;
-        const int r = p / C::KCH, c = wide_vk_chunk(r, p % C::KCH);
-        koff[u] = (uint32_t)r * (uint32_t)a.k_sn * 2u + 16u * (uint32_t)c;
-    }
-    // LDS-DMA of tile T into a stage by the pair T % 2: 18 buffer_load ...
-    // lds per wave, each 1 KB, counted by vmcnt (nothing else in the loop
-    // uses it)
-    auto dma_tile = [&](int T, int stage) __attribute__((always_inline)) {
-        if (sw || (T & 1) != cpair) return;
+        for (int u = 0; u < C::KWIN_W; ++u) {
+            const int p = (2 * u + cm) * 64 + lane;
+            const int r = p / C::KCH, c = wide_vk_chunk(r, p % C::KCH);
+            koff[u] = (uint32_t)r * (uint32_t)a.k_sn * 2u + 16u * (uint32_t)c;
+        }
+    };
+    // LDS-DMA of tile T into a stage by the pair T % 2 (value waves): 18
+    // buffer_load ... lds per wave, each 1 KB, counted by vmcnt (nothing else
+    // in the loop uses it)
+    auto dma_tile = [&](const uint32_t (&koff)[C::KWIN_W], int T, int stage) __attribute__((always_inline)) {
+        if ((T & 1) != cpair) return;
         const int rem = a.Nkv - T * TK;  // keys left, >= 1
         const u32x4 rk = buffer_rsrc(Kp + (int64_t)T * TK * a.k_sn,
                                      (uint32_t)(((int64_t)(rem - 1) * a.k_sn + DQK) * 2));
@@ -242,32 +245,22 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
 #pragma unroll
         for (int u = 0; u < C::KWIN_W; ++u) dma16_buf_to_lds(rk, koff[u], st + (2 * u + cm) * 1024);
     };
-    // this wave's LDS accesses are done, then every wave reaches this point
-    // (also a compiler memory barrier)
-    auto lds_barrier = [&]() __attribute__((always_inline)) {
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    };
-    // the same, where the pair that copies tile Tw first waits for all its
-    // copies (vmcnt(0): a partial count did not order the LDS-DMA writes);
-    // the barrier then publishes tile Tw to every wave
+    // the end of a tile for a value wave: the pair that copied tile Tw first
+    // waits for all its copies (vmcnt(0): a partial count did not order the
+    // LDS-DMA writes); the barrier then publishes tile Tw to every wave
     auto copy_barrier = [&](int Tw) __attribute__((always_inline)) {
-        if (!sw && (Tw & 1) == cpair)
+        if ((Tw & 1) == cpair)
             asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
         else
             lds_barrier();
     };
-
-    // ---- K fragment addresses: key row r = 16 kh + l16, chunk 4 ks + kg. With
-    // s = the row's swizzle, (4 ks + kg) ^ s = 4 (ks ^ s/4) + (kg ^ s%4), and
-    // s/4 < 2 only flips ks's low bit: fragment 2 j + b is at kb_b + 128 j. --
-    uint32_t kb[2];
-    {
-        const int r = 16 * kh + l16;
-        const int t = (r >> 1) & 7, s = t ^ ((t & 1) << 2);
-        const uint32_t base = (uint32_t)(uintptr_t)(lds_void *)lds + (uint32_t)(r * C::KROW_B + 16 * (kg ^ (s & 3)));
-        kb[0] = base + 64 * (0 ^ (s >> 2));
-        kb[1] = base + 64 * (1 ^ (s >> 2));
-    }
+    // tiles 0, 1, 2 into stages 0, 1, 2 (value waves), landed everywhere
+    auto prologue = [&](const uint32_t(&koff)[C::KWIN_W], bool copies) __attribute__((always_inline)) {
+        __syncthreads();  // the ring, the P buffers and the statistics are free
+        if (copies)
+            for (int T = 0; T < 3 && T < n_tiles; ++T) dma_tile(koff, T, T);
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    };
 
     // ---- P layout: row-major, 80-byte rows (conflict-free 16-byte reads of 16
     // rows); within each 16-key chunk key 4 q + i (q < 4, i < 4) sits at
@@ -277,65 +270,6 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
     const uint32_t p_wr = (uint32_t)(l16 + 16 * rh) * C::PROW_B + 2 * (16 * kh + 8 * (G & 1) + 4 * (G >> 1));
     const uint32_t p_rd = (uint32_t)l32 * C::PROW_B + 2 * 8 * g;
 
-    // ---- state -------------------------------------------------------------
-    f32x16 oacc[CBW];
-    float m = 0.f;  // reference of row srow (score*c units), same in both key halves
-    float l;        // normalizer of row srow over this lane's keys (score waves)
-    float *stat = (float *)(lds + C::SOFF);  // [kh][32] per-half row values, then m[32]
-
-    // ---- Vᵀ fragments (value columns 32 db .. 32 db + 31, db = 2w + i, keys
-    // 16 kc .. 16 kc + 15): two transposed reads (key halves hr) of the K tile,
-    // whose rows begin with the values. Lane (4 g + i16 / 4 + 8 hr + 16 kc,
-    // column 32 db + 16 (G % 2) + 4 (i16 % 4)) reads 4 values; the row's
-    // swizzle does not depend on kc, so (i, kc, hr) is at vtb[hr][i] + 16
-    // rows (kc). ------------------------------------------------------------
-    uint32_t vtb[2][CBW];
-    {
-        const int i16 = lane & 15;
-#pragma unroll
-        for (int hr = 0; hr < 2; ++hr)
-#pragma unroll
-            for (int i = 0; i < CBW; ++i) {
-                const int vr = 8 * hr + 4 * g + (i16 >> 2);
-                const int col = 32 * (CBW * w + i) + 16 * (G & 1) + 4 * (i16 & 3);
-                vtb[hr][i] = (uint32_t)(uintptr_t)(lds_void *)lds +
-                             (uint32_t)(vr * C::KROW_B + 16 * wide_vk_chunk(vr, col >> 3) + 2 * (col & 7));
-            }
-    }
-    auto vt_frag_k = [&](uint32_t stage_off, int i, int kc) __attribute__((always_inline)) {
-        i16x4 hv[2];
-#pragma unroll
-        for (int hr = 0; hr < 2; ++hr) {
-            const uint32_t addr = vtb[hr][i] + stage_off + 16 * C::KROW_B * kc;
-            hv[hr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(uintptr_t)addr);
-        }
-        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(hv[0], hv[1], 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-    // P·V of a tile in two parts: the LDS reads (P and the Vᵀ fragments) and
-    // the MFMAs, so that the next tile's score block can go between them
-    auto pv_reads = [&](const unsigned char *pb, int stage, bf16x8 (&pf)[2], bf16x8 (&vf)[2][CBW])
-                        __attribute__((always_inline)) {
-        const uint32_t stage_off = stage * C::KTILE_B;
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) pf[kc] = *(const bf16x8 *)(pb + p_rd + 32 * kc);
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-            for (int i = 0; i < CBW; ++i) vf[kc][i] = vt_frag_k(stage_off, i, kc);
-    };
-    auto pv_mma = [&](const bf16x8 (&pf)[2], const bf16x8 (&vf)[2][CBW]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-            for (int i = 0; i < CBW; ++i) oacc[i] = mfma_32x32x16(vf[kc][i], pf[kc], oacc[i]);
-    };
-    // maximum of this lane's block row over the 4 lanes that share it
-    auto block_row_max = [&](const float (&sv)[4]) __attribute__((always_inline)) {
-        float x = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-        x = fmaxf(x, __shfl_xor(x, 16));
-        x = fmaxf(x, __shfl_xor(x, 32));
-        return x;
-    };
     // combine a per-row value of the two key halves (score waves give it; one
     // barrier for all waves); returns v(half 0) op v(half 1) for row srow
     auto combine_halves = [&](float v, bool is_max) __attribute__((always_inline)) {
@@ -344,149 +278,250 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
         const float v0 = stat[16 * rh + l16], v1 = stat[32 + 16 * rh + l16];
         return is_max ? fmaxf(v0, v1) : v0 + v1;
     };
-    // the score block of tile T (its first K fragment reads issued), masked
-    auto scores = [&](int T, int stage, float (&sv)[4]) __attribute__((always_inline)) {
-        const uint32_t so = stage * C::KTILE_B;
-        const f32x4 sacc = wide_vk_qk(qf, kb[0] + so, kb[1] + so);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sv[i] = sacc[i];
-        if (T >= first_masked) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = T * TK + 16 * kh + 4 * G + i;
-                if ((CAUSAL && key > srow) || key >= a.Nkv) sv[i] = -INFINITY;
-            }
-        }
-    };
-    auto kreads0 = [&](int stage) __attribute__((always_inline)) {
-        const uint32_t so = stage * C::KTILE_B;
-        wide_vk_kreads0(kb[0] + so, kb[1] + so);
-    };
-    // P of the block (bf16) into tile T's P buffer, and l
-    auto block_p = [&](int T, const float (&sv)[4]) __attribute__((always_inline)) {
-        const float negm = -m;
-        const float e0 = exp2_hw(fmaf(sv[0], a.c, negm)), e1 = exp2_hw(fmaf(sv[1], a.c, negm));
-        const float e2 = exp2_hw(fmaf(sv[2], a.c, negm)), e3 = exp2_hw(fmaf(sv[3], a.c, negm));
-        const uint32_t p01 = pack_bf16x2(e0, e1), p23 = pack_bf16x2(e2, e3);
-        l = sum_bf16x2(p23, sum_bf16x2(p01, l));
-        *(u32x2 *)(lds + C::POFF + (T & 1) * C::PBUF_B + p_wr) = u32x2{p01, p23};
-    };
-    // tiles 0, 1, 2 into stages 0, 1, 2, landed everywhere; the score waves'
-    // first K fragment reads issued
-    auto prologue = [&]() __attribute__((always_inline)) {
-        __syncthreads();  // the ring, the P buffers and the statistics are free
-        for (int T = 0; T < 3 && T < n_tiles; ++T) dma_tile(T, T);
-        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-        if (sw) kreads0(0);
-    };
-
-    // ---- one pass over the keys: O and l (set_m: the reference from tile 0)
-    // Tile T's stage is T % 4. Software pipeline, one barrier per tile:
-    //   [P·V reads of T] [K reads of T + 1 | copy of T + 3] [scores of T + 1]
-    //   [P·V MFMAs of T] [P of T + 1] barrier
-    // The copy of T + 3 goes into the stage of tile T - 1, which every wave
-    // finished before this tile's barrier; the barrier at the end publishes
-    // tile T + 2, whose copies were issued two tiles earlier.
-    auto pass = [&](bool set_m) __attribute__((always_inline)) {
-        l = 0.f;
-#pragma unroll
-        for (int i = 0; i < CBW; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
-        prologue();
-        {
-            float sv[4] = {0.f, 0.f, 0.f, 0.f};
-            if (sw) scores(0, 0, sv);
-            if (set_m) {
-                // reference: the row maximum over tile 0 (an extra barrier,
-                // the same in every wave)
-                const float mx = combine_halves(sw ? block_row_max(sv) : 0.f, true) * a.c;
-                m = (mx == -INFINITY) ? 0.f : mx;
-            }
-            if (sw) block_p(0, sv);
-            lds_barrier();  // tile 1 landed in the prologue
-        }
-        for (int T = 0; T < n_tiles; ++T) {
-            const bool more = T + 1 < n_tiles;
-            bf16x8 pf[2], vf[2][CBW];
-            pv_reads(lds + C::POFF + (T & 1) * C::PBUF_B, T & 3, pf, vf);
-            if (sw && more) kreads0((T + 1) & 3);
-            if (T + 3 < n_tiles) dma_tile(T + 3, (T + 3) & 3);
-            float sv[4] = {0.f, 0.f, 0.f, 0.f};
-            if (sw && more) scores(T + 1, (T + 1) & 3, sv);
-            pv_mma(pf, vf);
-            if (more) {
-                if (sw) block_p(T + 1, sv);
-                copy_barrier(T + 2);
-            }
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no copy outlives the pass
-    };
-    // exact row maxima (in score*c units; score waves), no P·V; one barrier
-    // per tile as above
-    auto max_pass = [&]() __attribute__((always_inline)) {
-        float M = -INFINITY;
-        prologue();
-        for (int T = 0; T < n_tiles; ++T) {
-            if (sw) {
-                float sv[4];
-                scores(T, T & 3, sv);
-                M = fmaxf(M, block_row_max(sv) * a.c);
-            }
-            if (T + 3 < n_tiles) dma_tile(T + 3, (T + 3) & 3);
-            copy_barrier(T + 1);
-            if (sw && T + 1 < n_tiles) kreads0((T + 1) & 3);
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        return M;
-    };
-
-    // per-row l of the whole row (both halves, all lanes), for row l32 of the
-    // epilogue; m of row l32 likewise
-    auto finish_stats = [&](float &l_out, float &m_out) __attribute__((always_inline)) {
-        float x = l;
+    // per-row l of the whole row (both halves), for row l32 of the epilogue,
+    // and m of that row: score waves give their l_part and m, every wave gets
+    // the results
+    auto finish_stats = [&](float l_part, float m_srow, float &l_out, float &m_out)
+                            __attribute__((always_inline)) {
+        float x = l_part;
         x += __shfl_xor(x, 16);
         x += __shfl_xor(x, 32);
         __syncthreads();  // the statistics area is free
         if (sw && G == 0) {
             stat[32 * kh + 16 * rh + l16] = x;
-            if (kh == 0) stat[64 + 16 * rh + l16] = m;
+            if (kh == 0) stat[64 + 16 * rh + l16] = m_srow;
         }
         __syncthreads();
         l_out = stat[l32] + stat[32 + l32];
         m_out = stat[64 + l32];
     };
-
     constexpr float kMaxL = 4294967296.0f;  // 2^32: every p <= 2^32 when l <= 2^32
-    pass(true);
-    float l_row, m_row;
-    finish_stats(l_row, m_row);
-    // every wave holds the same 32 rows' normalizers
-    const bool bad = __builtin_amdgcn_ballot_w64(!(l_row <= kMaxL)) != 0;
-    if (bad) {
-        // exact row maxima, then the pass again (rare)
-        float M = max_pass();
-        __syncthreads();
-        M = combine_halves(M, true);
-        m = (M == -INFINITY) ? 0.f : M;
-        pass(false);
-        finish_stats(l_row, m_row);
-    }
+    // every wave holds the same 32 rows' normalizers, so the whole workgroup
+    // takes the same decision
+    auto needs_exact = [&](float l_row) __attribute__((always_inline)) {
+        return __builtin_amdgcn_ballot_w64(!(l_row <= kMaxL)) != 0;
+    };
 
-    // ---- O = Oᵀ / l (one reciprocal per row), logsumexp ---------------------
-    const float inv_l = 1.0f / l_row;
-    if (row < a.Nq) {
-        __bf16 *orow = Op + (int64_t)row * a.o_sn;
+    // The two roles run separate code from here on (so that each keeps only
+    // its own registers live), with the same sequence of barriers:
+    //   pass: prologue barrier, [tile-0 reference: one barrier], the barrier
+    //   after P(0), then one barrier per tile T < n_tiles - 1;
+    //   stats: two; if some row needs exact maxima: the max pass (prologue,
+    //   one per tile), one, the pass again, stats again.
+    // Per tile T the score waves compute the scores of tile T + 1 and write
+    // its P while the value waves run P·V of tile T and copy tile T + 3; on
+    // each SIMD one wave of each kind, so the MFMAs of the two overlap.
+    if (sw) {
+        // ================= score waves =================
+        // K fragment addresses: key row r = 16 kh + l16, chunk 4 ks + kg.
+        // With s = the row's swizzle, (4 ks + kg) ^ s = 4 (ks ^ s/4) +
+        // (kg ^ s%4), and s/4 < 2 only flips ks's low bit: fragment 2 j + b
+        // is at kb_b + 128 j.
+        uint32_t kb[2];
+        {
+            const int r = 16 * kh + l16;
+            const int t = (r >> 1) & 7, s = t ^ ((t & 1) << 2);
+            const uint32_t base = (uint32_t)(uintptr_t)(lds_void *)lds + (uint32_t)(r * C::KROW_B + 16 * (kg ^ (s & 3)));
+            kb[0] = base + 64 * (0 ^ (s >> 2));
+            kb[1] = base + 64 * (1 ^ (s >> 2));
+        }
+        // Q of the block's 16 rows (B operands), loaded at the start of each
+        // pass so that it is live in this role's code only
+        bf16x8 qf[C::NKS];
+        auto load_q = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < CBW; ++i)
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int col = 32 * (CBW * w + i) + acc_row(4 * rr, g);
-                store4(orow + col, oacc[i][4 * rr] * inv_l, oacc[i][4 * rr + 1] * inv_l,
-                       oacc[i][4 * rr + 2] * inv_l, oacc[i][4 * rr + 3] * inv_l);
+            for (int ks = 0; ks < C::NKS; ++ks) {
+                u32x4 v = {0, 0, 0, 0};
+                if (srow < a.Nq) v = load8_bf16(Qp + (int64_t)srow * a.q_sn + 32 * ks + 8 * kg);
+                qf[ks] = u32x4_as_bf16x8(v);
             }
-        if (w == 0 && g == 0 && a.lse)
-            a.lse[((int64_t)b * a.Hq + h) * a.Nq + row] = (m_row + log2f(l_row)) * 0.69314718055994531f;
+        };
+        float m = 0.f;  // reference of row srow (score*c units), same in both key halves
+        float l = 0.f;  // normalizer of row srow over this lane's keys
+        auto kreads0 = [&](int stage) __attribute__((always_inline)) {
+            const uint32_t so = stage * C::KTILE_B;
+            wide_vk_kreads0(kb[0] + so, kb[1] + so);
+        };
+        // the score block of tile T (its first K fragment reads issued), masked
+        auto scores = [&](int T, int stage, float (&sv)[4]) __attribute__((always_inline)) {
+            const uint32_t so = stage * C::KTILE_B;
+            const f32x4 sacc = wide_vk_qk(qf, kb[0] + so, kb[1] + so);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sv[i] = sacc[i];
+            if (T >= first_masked) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = T * TK + 16 * kh + 4 * G + i;
+                    if ((CAUSAL && key > srow) || key >= a.Nkv) sv[i] = -INFINITY;
+                }
+            }
+        };
+        // maximum of this lane's block row over the 4 lanes that share it
+        auto block_row_max = [&](const float (&sv)[4]) __attribute__((always_inline)) {
+            float x = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+            x = fmaxf(x, __shfl_xor(x, 16));
+            x = fmaxf(x, __shfl_xor(x, 32));
+            return x;
+        };
+        // P of the block (bf16) into tile T's P buffer, and l
+        auto block_p = [&](int T, const float (&sv)[4]) __attribute__((always_inline)) {
+            const float negm = -m;
+            const float e0 = exp2_hw(fmaf(sv[0], a.c, negm)), e1 = exp2_hw(fmaf(sv[1], a.c, negm));
+            const float e2 = exp2_hw(fmaf(sv[2], a.c, negm)), e3 = exp2_hw(fmaf(sv[3], a.c, negm));
+            const uint32_t p01 = pack_bf16x2(e0, e1), p23 = pack_bf16x2(e2, e3);
+            l = sum_bf16x2(p23, sum_bf16x2(p01, l));
+            *(u32x2 *)(lds + C::POFF + (T & 1) * C::PBUF_B + p_wr) = u32x2{p01, p23};
+        };
+        const uint32_t no_koff[C::KWIN_W] = {};
+        auto pass = [&](bool set_m) __attribute__((always_inline)) {
+            l = 0.f;
+            load_q();
+            prologue(no_koff, false);
+            kreads0(0);
+            {
+                float sv[4];
+                scores(0, 0, sv);
+                if (set_m) {
+                    // reference: the row maximum over tile 0
+                    const float mx = combine_halves(block_row_max(sv), true) * a.c;
+                    m = (mx == -INFINITY) ? 0.f : mx;
+                }
+                block_p(0, sv);
+                lds_barrier();  // P(0) written; tile 1 landed in the prologue
+            }
+            for (int T = 0; T + 1 < n_tiles; ++T) {
+                float sv[4];
+                kreads0((T + 1) & 3);
+                scores(T + 1, (T + 1) & 3, sv);
+                block_p(T + 1, sv);
+                lds_barrier();  // the copy barrier of tile T + 2
+            }
+        };
+        // exact row maxima (in score*c units), no P·V; one barrier per tile
+        auto max_pass = [&]() __attribute__((always_inline)) {
+            float M = -INFINITY;
+            load_q();
+            prologue(no_koff, false);
+            kreads0(0);
+            for (int T = 0; T < n_tiles; ++T) {
+                float sv[4];
+                scores(T, T & 3, sv);
+                M = fmaxf(M, block_row_max(sv) * a.c);
+                lds_barrier();
+                if (T + 1 < n_tiles) kreads0((T + 1) & 3);
+            }
+            return M;
+        };
+        pass(true);
+        float l_row, m_row;
+        finish_stats(l, m, l_row, m_row);
+        if (needs_exact(l_row)) {
+            float M = max_pass();
+            __syncthreads();
+            M = combine_halves(M, true);
+            m = (M == -INFINITY) ? 0.f : M;
+            pass(false);
+            finish_stats(l, m, l_row, m_row);
+        }
+    } else {
+        // ================= value waves =================
+        uint32_t koff[C::KWIN_W];
+        copy_offsets(koff);
+        // Vᵀ fragments (value columns 32 db .. 32 db + 31, db = 4 vw + i, keys
+        // 16 kc .. 16 kc + 15): two transposed reads (key halves hr) of the K
+        // tile, whose rows begin with the values. Lane (4 g + i16 / 4 + 8 hr +
+        // 16 kc, column 32 db + 16 (G % 2) + 4 (i16 % 4)) reads 4 values; the
+        // row's swizzle does not depend on kc, so (i, kc, hr) is at
+        // vtb[hr][i] + 16 rows (kc).
+        uint32_t vtb[2][CBW];
+        {
+            const int i16 = lane & 15;
+#pragma unroll
+            for (int hr = 0; hr < 2; ++hr)
+#pragma unroll
+                for (int i = 0; i < CBW; ++i) {
+                    const int vr = 8 * hr + 4 * g + (i16 >> 2);
+                    const int col = 32 * (CBW * vw + i) + 16 * (G & 1) + 4 * (i16 & 3);
+                    vtb[hr][i] = (uint32_t)(uintptr_t)(lds_void *)lds +
+                                 (uint32_t)(vr * C::KROW_B + 16 * wide_vk_chunk(vr, col >> 3) + 2 * (col & 7));
+                }
+        }
+        auto vt_frag_k = [&](uint32_t stage_off, int i, int kc) __attribute__((always_inline)) {
+            i16x4 hv[2];
+#pragma unroll
+            for (int hr = 0; hr < 2; ++hr) {
+                const uint32_t addr = vtb[hr][i] + stage_off + 16 * C::KROW_B * kc;
+                hv[hr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(uintptr_t)addr);
+            }
+            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(hv[0], hv[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        f32x16 oacc[CBW];
+        // O += P·V of tile T: P from its buffer, V from its stage; the copy
+        // of tile T + 3 goes between the LDS reads and the MFMAs
+        auto pv_tile = [&](int T) __attribute__((always_inline)) {
+            const unsigned char *pb = lds + C::POFF + (T & 1) * C::PBUF_B;
+            const uint32_t stage_off = (T & 3) * C::KTILE_B;
+            bf16x8 pf[2], vf[2][CBW];
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc) pf[kc] = *(const bf16x8 *)(pb + p_rd + 32 * kc);
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+                for (int i = 0; i < CBW; ++i) vf[kc][i] = vt_frag_k(stage_off, i, kc);
+            if (T + 3 < n_tiles) dma_tile(koff, T + 3, (T + 3) & 3);
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+                for (int i = 0; i < CBW; ++i) oacc[i] = mfma_32x32x16(vf[kc][i], pf[kc], oacc[i]);
+        };
+        auto pass = [&](bool set_m) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < CBW; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
+            prologue(koff, true);
+            if (set_m) combine_halves(0.f, true);  // the score waves' reference barrier
+            lds_barrier();                         // P(0) written
+            for (int T = 0; T < n_tiles; ++T) {
+                pv_tile(T);
+                if (T + 1 < n_tiles) copy_barrier(T + 2);
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no copy outlives the pass
+        };
+        auto max_pass = [&]() __attribute__((always_inline)) {
+            prologue(koff, true);
+            for (int T = 0; T < n_tiles; ++T) {
+                if (T + 3 < n_tiles) dma_tile(koff, T + 3, (T + 3) & 3);
+                copy_barrier(T + 1);
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        };
+        pass(true);
+        float l_row, m_row;
+        finish_stats(0.f, 0.f, l_row, m_row);
+        if (needs_exact(l_row)) {
+            max_pass();
+            __syncthreads();
+            combine_halves(0.f, true);
+            pass(false);
+            finish_stats(0.f, 0.f, l_row, m_row);
+        }
+
+        // ---- O = Oᵀ / l (one reciprocal per row), logsumexp -----------------
+        const float inv_l = 1.0f / l_row;
+        if (row < a.Nq) {
+            __bf16 *orow = Op + (int64_t)row * a.o_sn;
+#pragma unroll
+            for (int i = 0; i < CBW; ++i)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int col = 32 * (CBW * vw + i) + acc_row(4 * rr, g);
+                    store4(orow + col, oacc[i][4 * rr] * inv_l, oacc[i][4 * rr + 1] * inv_l,
+                           oacc[i][4 * rr + 2] * inv_l, oacc[i][4 * rr + 3] * inv_l);
+                }
+            if (vw == 0 && g == 0 && a.lse)
+                a.lse[((int64_t)b * a.Hq + h) * a.Nq + row] = (m_row + log2f(l_row)) * 0.69314718055994531f;
+        }
     }
 #endif
 }
