@@ -11,12 +11,12 @@
 //    16 kh .. 16 kh + 15 and rows 16 rh .. 16 rh + 15 and compute it whole
 //    (Sᵀ = K·Qᵀ, 18 k-steps of v_mfma_f32_16x16x32_bf16, their 16 rows of Q
 //    held in registers), apply the mask and the exponential to it and write
-//    P (bf16) to LDS.
-//  * Value waves 4..7 (vw = w - 4) move the K tiles into LDS (LDS-DMA) and,
-//    after the barrier that publishes a tile's P, read all of it and
-//    accumulate output columns 128 vw .. 128 vw + 127 for all 32 rows
-//    (O = P·V split over the value columns), reading their Vᵀ fragments from
-//    the K tile.
+//    P (bf16) to LDS. They also move the K tiles into LDS (LDS-DMA), after
+//    writing P, in the time they would otherwise wait at the barrier.
+//  * Value waves 4..7 (vw = w - 4), after the barrier that publishes a
+//    tile's P, read all of it and accumulate output columns 128 vw ..
+//    128 vw + 127 for all 32 rows (O = P·V split over the value columns),
+//    reading their Vᵀ fragments from the K tile.
 //  Each SIMD holds one score wave and one value wave: in each tile period
 //  the score wave's MFMAs for tile T + 1 and the value wave's for tile T
 //  share the SIMD's matrix pipe (18 16x16 + 8 32x32 MFMAs), and each wave's
@@ -27,13 +27,13 @@
 //  * Row statistics: the reference m of a row (the maximum over the first 32
 //    keys) and, at the end, its normalizer l are the two key halves' values
 //    combined through LDS.
-//  * K tiles (32 keys x 1152 bytes) sit in a four-stage LDS ring: after tile
-//    T's barrier one pair of value waves issues tile T + 3 (the pairs take
-//    turns), and the barrier two tiles later waits for it.
+//  * K tiles (32 keys x 1152 bytes) sit in a four-stage LDS ring: in the
+//    period after tile T's barrier one pair of score waves issues tile T + 3
+//    (the pairs take turns), and the barrier two tiles later waits for it.
 //  * Software pipeline, one barrier per tile: after the barrier that
 //    publishes P of tile T, the score waves read K of tile T + 1, run its
-//    score MFMAs and write its P; the value waves read P and Vᵀ of tile T,
-//    issue the copy of tile T + 3 and run the P·V MFMAs of T.
+//    score MFMAs, write its P and issue the copy of tile T + 3; the value
+//    waves read P and Vᵀ of tile T and run its P·V MFMAs.
 //  * K rows are 72 16-byte chunks. Chunk c of row r is stored at
 //    c ^ s(r), s(r) = t ^ 4 (t & 1), t = (r / 2) % 8; with the k-group
 //    order below the 16 lanes served together by a fragment read
@@ -65,9 +65,9 @@ struct WideVkCfg {
     static constexpr int POFF = NSTAGE * KTILE_B;  // P buffers after the ring
     static constexpr int SOFF = POFF + 2 * PBUF_B; // row statistics: [2 key halves][32 rows] + m[32]
     static constexpr int LDS_BYTES = SOFF + 3 * TQ * 4;
-    static constexpr int KWIN_W = KTILE_B / 1024 / 2;  // 1 KB copies per copy wave per copied tile
+    static constexpr int KWIN_W = KTILE_B / 1024 / 2;  // 1 KB copies per copying wave per copied tile
     static constexpr int CBW = DV / 32 / (NWAVE - NSW);            // 32-column blocks of O per value wave
-    static_assert(NWAVE - NSW == 4, "two pairs of copy waves");
+    static_assert(NSW == 4 && NWAVE - NSW == 4, "four score waves (two copy pairs), four value waves");
     static_assert(KTILE_B % 2048 == 0, "tile pieces must split over a pair of copy waves");
     static_assert(NKS == 18, "the score block is written for 18 k-steps");
     static_assert(KCH % 8 == 0, "the swizzle permutes aligned groups of 8 chunks");
@@ -215,7 +215,7 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
     };
     float *stat = (float *)(lds + C::SOFF);  // [kh][32] per-half row values, then m[32]
 
-    // ---- K copies (value waves): waves 4, 5 copy the even tiles, 6, 7 the
+    // ---- K copies (score waves): waves 0, 1 copy the even tiles, 2, 3 the
     // odd ones, so that a pair's copies of a tile are its only ones in flight
     // when it waits for them (vmcnt(0)) two tiles later. Piece u of pair
     // member cm is the 1 KB at (2u + cm) KB of the tile; lane i moves its
@@ -223,7 +223,7 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
     // swizzle puts there. The byte offsets inside a tile are the same for
     // every tile; the copies go through a buffer resource that ends at the
     // last key, so rows past it read as zeros (finite, masked). ----------
-    const int cpair = vw >> 1, cm = vw & 1;
+    const int cpair = (w >> 1) & 1, cm = w & 1;  // score waves' copy pair
     auto copy_offsets = [&](uint32_t (&koff)[C::KWIN_W]) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < C::KWIN_W; ++u) {
@@ -232,20 +232,23 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
             koff[u] = (uint32_t)r * (uint32_t)a.k_sn * 2u + 16u * (uint32_t)c;
         }
     };
-    // LDS-DMA of tile T into a stage by the pair T % 2 (value waves): 18
+    // LDS-DMA of tile T into a stage by the pair T % 2 (score waves): 18
     // buffer_load ... lds per wave, each 1 KB, counted by vmcnt (nothing else
-    // in the loop uses it)
+    // in the loop uses it). T is uniform; the resource is made explicitly so
+    // (readfirstlane), as the instruction takes it in scalar registers.
     auto dma_tile = [&](const uint32_t (&koff)[C::KWIN_W], int T, int stage) __attribute__((always_inline)) {
         if ((T & 1) != cpair) return;
         const int rem = a.Nkv - T * TK;  // keys left, >= 1
-        const u32x4 rk = buffer_rsrc(Kp + (int64_t)T * TK * a.k_sn,
-                                     (uint32_t)(((int64_t)(rem - 1) * a.k_sn + DQK) * 2));
+        u32x4 rk = buffer_rsrc(Kp + (int64_t)T * TK * a.k_sn,
+                               (uint32_t)(((int64_t)(rem - 1) * a.k_sn + DQK) * 2));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rk[i] = __builtin_amdgcn_readfirstlane(rk[i]);
         unsigned char *st = lds + stage * C::KTILE_B;
         perturb_pause();
 #pragma unroll
         for (int u = 0; u < C::KWIN_W; ++u) dma16_buf_to_lds(rk, koff[u], st + (2 * u + cm) * 1024);
     };
-    // the end of a tile for a value wave: the pair that copied tile Tw first
+    // the end of a tile for a score wave: the pair that copied tile Tw first
     // waits for all its copies (vmcnt(0): a partial count did not order the
     // LDS-DMA writes); the barrier then publishes tile Tw to every wave
     auto copy_barrier = [&](int Tw) __attribute__((always_inline)) {
@@ -254,7 +257,7 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
         else
             lds_barrier();
     };
-    // tiles 0, 1, 2 into stages 0, 1, 2 (value waves), landed everywhere
+    // tiles 0, 1, 2 into stages 0, 1, 2 (score waves), landed everywhere
     auto prologue = [&](const uint32_t(&koff)[C::KWIN_W], bool copies) __attribute__((always_inline)) {
         __syncthreads();  // the ring, the P buffers and the statistics are free
         if (copies)
@@ -308,9 +311,9 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
     //   after P(0), then one barrier per tile T < n_tiles - 1;
     //   stats: two; if some row needs exact maxima: the max pass (prologue,
     //   one per tile), one, the pass again, stats again.
-    // Per tile T the score waves compute the scores of tile T + 1 and write
-    // its P while the value waves run P·V of tile T and copy tile T + 3; on
-    // each SIMD one wave of each kind, so the MFMAs of the two overlap.
+    // Per tile T the score waves compute the scores of tile T + 1, write its
+    // P and copy tile T + 3 while the value waves run P·V of tile T; on each
+    // SIMD one wave of each kind, so the MFMAs of the two overlap.
     if (sw) {
         // ================= score waves =================
         // K fragment addresses: key row r = 16 kh + l16, chunk 4 ks + kg.
@@ -372,11 +375,12 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
             l = sum_bf16x2(p23, sum_bf16x2(p01, l));
             *(u32x2 *)(lds + C::POFF + (T & 1) * C::PBUF_B + p_wr) = u32x2{p01, p23};
         };
-        const uint32_t no_koff[C::KWIN_W] = {};
+        uint32_t koff[C::KWIN_W];
+        copy_offsets(koff);
         auto pass = [&](bool set_m) __attribute__((always_inline)) {
             l = 0.f;
             load_q();
-            prologue(no_koff, false);
+            prologue(koff, true);
             kreads0(0);
             {
                 float sv[4];
@@ -394,22 +398,26 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
                 kreads0((T + 1) & 3);
                 scores(T + 1, (T + 1) & 3, sv);
                 block_p(T + 1, sv);
-                lds_barrier();  // the copy barrier of tile T + 2
+                if (T + 3 < n_tiles) dma_tile(koff, T + 3, (T + 3) & 3);
+                copy_barrier(T + 2);
             }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no copy outlives the pass
         };
         // exact row maxima (in score*c units), no P·V; one barrier per tile
         auto max_pass = [&]() __attribute__((always_inline)) {
             float M = -INFINITY;
             load_q();
-            prologue(no_koff, false);
+            prologue(koff, true);
             kreads0(0);
             for (int T = 0; T < n_tiles; ++T) {
                 float sv[4];
                 scores(T, T & 3, sv);
                 M = fmaxf(M, block_row_max(sv) * a.c);
-                lds_barrier();
+                if (T + 3 < n_tiles) dma_tile(koff, T + 3, (T + 3) & 3);
+                copy_barrier(T + 1);
                 if (T + 1 < n_tiles) kreads0((T + 1) & 3);
             }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             return M;
         };
         pass(true);
@@ -425,8 +433,7 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
         }
     } else {
         // ================= value waves =================
-        uint32_t koff[C::KWIN_W];
-        copy_offsets(koff);
+        const uint32_t koff[C::KWIN_W] = {};
         // Vᵀ fragments (value columns 32 db .. 32 db + 31, db = 4 vw + i, keys
         // 16 kc .. 16 kc + 15): two transposed reads (key halves hr) of the K
         // tile, whose rows begin with the values. Lane (4 g + i16 / 4 + 8 hr +
@@ -468,7 +475,6 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
             for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
                 for (int i = 0; i < CBW; ++i) vf[kc][i] = vt_frag_k(stage_off, i, kc);
-            if (T + 3 < n_tiles) dma_tile(koff, T + 3, (T + 3) & 3);
 #pragma unroll
             for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
@@ -479,22 +485,17 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
             for (int i = 0; i < CBW; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
-            prologue(koff, true);
+            prologue(koff, false);
             if (set_m) combine_halves(0.f, true);  // the score waves' reference barrier
             lds_barrier();                         // P(0) written
             for (int T = 0; T < n_tiles; ++T) {
                 pv_tile(T);
-                if (T + 1 < n_tiles) copy_barrier(T + 2);
+                if (T + 1 < n_tiles) lds_barrier();
             }
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no copy outlives the pass
         };
         auto max_pass = [&]() __attribute__((always_inline)) {
-            prologue(koff, true);
-            for (int T = 0; T < n_tiles; ++T) {
-                if (T + 3 < n_tiles) dma_tile(koff, T + 3, (T + 3) & 3);
-                copy_barrier(T + 1);
-            }
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            prologue(koff, false);
+            for (int T = 0; T < n_tiles; ++T) lds_barrier();
         };
         pass(true);
         float l_row, m_row;
