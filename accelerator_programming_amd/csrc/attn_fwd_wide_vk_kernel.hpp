@@ -165,6 +165,60 @@ __device__ __forceinline__ f32x4 wide_vk_qk(const bf16x8 (&q)[18], uint32_t kb0,
     return s + t;
 }
 
+// The same score block with the LDS-DMA of one K tile's share of a copying
+// wave (18 x 1 KB) interleaved: DMA u right after the MFMA of k-step u, so
+// that the copies reach the memory pipeline at the pace it takes them
+// instead of as a burst that would stall the wave (about 16 cycles per 1 KB
+// copy per CU). DMA u lands at LDS byte address mb + 2048 u; M0 is written
+// inside the statement, each DMA followed by a wait state before the next
+// M0 write. The copies are counted by vmcnt only, so the lgkmcnt waits of
+// the block are unchanged.
+#define WIDE_VK_DMA0 "s_add_u32 m0, %[mb], 0\n\tbuffer_load_dwordx4 %[o0], %[rk], 0 offen lds\n\ts_nop 0\n\t"
+#define WIDE_VK_DMA1 "s_add_u32 m0, %[mb], 2048\n\tbuffer_load_dwordx4 %[o1], %[rk], 0 offen lds\n\ts_nop 0\n\t"
+#define WIDE_VK_DMA2 "s_add_u32 m0, %[mb], 4096\n\tbuffer_load_dwordx4 %[o2], %[rk], 0 offen lds\n\ts_nop 0\n\t"
+#define WIDE_VK_DMA3 "s_add_u32 m0, %[mb], 6144\n\tbuffer_load_dwordx4 %[o3], %[rk], 0 offen lds\n\ts_nop 0\n\t"
+#define WIDE_VK_DMA4 "s_add_u32 m0, %[mb], 8192\n\tbuffer_load_dwordx4 %[o4], %[rk], 0 offen lds\n\ts_nop 0\n\t"
+#define WIDE_VK_DMA5 "s_add_u32 m0, %[mb], 10240\n\tbuffer_load_dwordx4 %[o5], %[rk], 0 offen lds\n\ts_nop 0\n\t"
+#define WIDE_VK_DMA6 "s_add_u32 m0, %[mb], 12288\n\tbuffer_load_dwordx4 %[o6], %[rk], 0 offen lds\n\ts_nop 0\n\t"
+#define WIDE_VK_DMA7 "s_add_u32 m0, %[mb], 14336\n\tbuffer_load_dwordx4 %[o7], %[rk], 0 offen lds\n\ts_nop 0\n\t"
+#define WIDE_VK_DMA8 "s_add_u32 m0, %[mb], 16384\n\tbuffer_load_dwordx4 %[o8], %[rk], 0 offen lds\n\ts_nop 0\n\t"
+#define WIDE_VK_DMA9 "s_add_u32 m0, %[mb], 18432\n\tbuffer_load_dwordx4 %[o9], %[rk], 0 offen lds\n\ts_nop 0\n\t"
+#define WIDE_VK_DMA10 "s_add_u32 m0, %[mb], 20480\n\tbuffer_load_dwordx4 %[o10], %[rk], 0 offen lds\n\ts_nop 0\n\t"
+#define WIDE_VK_DMA11 "s_add_u32 m0, %[mb], 22528\n\tbuffer_load_dwordx4 %[o11], %[rk], 0 offen lds\n\ts_nop 0\n\t"
+#define WIDE_VK_DMA12 "s_add_u32 m0, %[mb], 24576\n\tbuffer_load_dwordx4 %[o12], %[rk], 0 offen lds\n\ts_nop 0\n\t"
+#define WIDE_VK_DMA13 "s_add_u32 m0, %[mb], 26624\n\tbuffer_load_dwordx4 %[o13], %[rk], 0 offen lds\n\ts_nop 0\n\t"
+#define WIDE_VK_DMA14 "s_add_u32 m0, %[mb], 28672\n\tbuffer_load_dwordx4 %[o14], %[rk], 0 offen lds\n\ts_nop 0\n\t"
+#define WIDE_VK_DMA15 "s_add_u32 m0, %[mb], 30720\n\tbuffer_load_dwordx4 %[o15], %[rk], 0 offen lds\n\ts_nop 0\n\t"
+#define WIDE_VK_DMA16 "s_add_u32 m0, %[mb], 32768\n\tbuffer_load_dwordx4 %[o16], %[rk], 0 offen lds\n\ts_nop 0\n\t"
+#define WIDE_VK_DMA17 "s_add_u32 m0, %[mb], 34816\n\tbuffer_load_dwordx4 %[o17], %[rk], 0 offen lds\n\ts_nop 0\n\t"
+
+__device__ __forceinline__ f32x4 wide_vk_qk_copy(const bf16x8 (&q)[18], uint32_t kb0, uint32_t kb1,
+                                                 const uint32_t (&o)[18], u32x4 rk, uint32_t mb) {
+    f32x4 s, t;
+    asm volatile(WIDE_VK_MM0 WIDE_VK_DMA0 WIDE_VK_KR6 WIDE_VK_MM1 WIDE_VK_DMA1 WIDE_VK_KR7
+                 WIDE_VK_MM2 WIDE_VK_DMA2 WIDE_VK_KR8 WIDE_VK_MM3 WIDE_VK_DMA3 WIDE_VK_KR9
+                 WIDE_VK_MM4 WIDE_VK_DMA4 WIDE_VK_KR10 WIDE_VK_MM5 WIDE_VK_DMA5 WIDE_VK_KR11
+                 WIDE_VK_MM6 WIDE_VK_DMA6 WIDE_VK_KR12 WIDE_VK_MM7 WIDE_VK_DMA7 WIDE_VK_KR13
+                 WIDE_VK_MM8 WIDE_VK_DMA8 WIDE_VK_KR14 WIDE_VK_MM9 WIDE_VK_DMA9 WIDE_VK_KR15
+                 WIDE_VK_MM10 WIDE_VK_DMA10 WIDE_VK_KR16 WIDE_VK_MM11 WIDE_VK_DMA11 WIDE_VK_KR17
+                 WIDE_VK_MM12 WIDE_VK_DMA12 WIDE_VK_MM13 WIDE_VK_DMA13 WIDE_VK_MM14 WIDE_VK_DMA14
+                 WIDE_VK_MM15 WIDE_VK_DMA15 WIDE_VK_MM16 WIDE_VK_DMA16 WIDE_VK_MM17 WIDE_VK_DMA17
+                 "s_nop 7\n\ts_nop 7\n\ts_nop 3"
+                 : [s] "=&v"(s), [t] "=&v"(t)
+                 : [kb0] "v"(kb0), [kb1] "v"(kb1),
+                   [q0] "v"(q[0]), [q1] "v"(q[1]), [q2] "v"(q[2]), [q3] "v"(q[3]), [q4] "v"(q[4]),
+                   [q5] "v"(q[5]), [q6] "v"(q[6]), [q7] "v"(q[7]), [q8] "v"(q[8]), [q9] "v"(q[9]),
+                   [q10] "v"(q[10]), [q11] "v"(q[11]), [q12] "v"(q[12]), [q13] "v"(q[13]),
+                   [q14] "v"(q[14]), [q15] "v"(q[15]), [q16] "v"(q[16]), [q17] "v"(q[17]),
+                   [mb] "s"(mb), [rk] "s"(rk),
+                   [o0] "v"(o[0]), [o1] "v"(o[1]), [o2] "v"(o[2]), [o3] "v"(o[3]), [o4] "v"(o[4]),
+                   [o5] "v"(o[5]), [o6] "v"(o[6]), [o7] "v"(o[7]), [o8] "v"(o[8]), [o9] "v"(o[9]),
+                   [o10] "v"(o[10]), [o11] "v"(o[11]), [o12] "v"(o[12]), [o13] "v"(o[13]),
+                   [o14] "v"(o[14]), [o15] "v"(o[15]), [o16] "v"(o[16]), [o17] "v"(o[17])
+                 : WIDE_VK_CLOBBERS, "memory", "scc");
+    return s + t;
+}
+
 template <int DQK, int DV, bool CAUSAL>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 __attribute__((amdgpu_num_vgpr(176)))  // v176 .. v199: the K fragment ring of the asm blocks
@@ -236,13 +290,17 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
     // buffer_load ... lds per wave, each 1 KB, counted by vmcnt (nothing else
     // in the loop uses it). T is uniform; the resource is made explicitly so
     // (readfirstlane), as the instruction takes it in scalar registers.
-    auto dma_tile = [&](const uint32_t (&koff)[C::KWIN_W], int T, int stage) __attribute__((always_inline)) {
-        if ((T & 1) != cpair) return;
+    auto tile_rsrc = [&](int T) __attribute__((always_inline)) {
         const int rem = a.Nkv - T * TK;  // keys left, >= 1
         u32x4 rk = buffer_rsrc(Kp + (int64_t)T * TK * a.k_sn,
                                (uint32_t)(((int64_t)(rem - 1) * a.k_sn + DQK) * 2));
 #pragma unroll
         for (int i = 0; i < 4; ++i) rk[i] = __builtin_amdgcn_readfirstlane(rk[i]);
+        return rk;
+    };
+    auto dma_tile = [&](const uint32_t (&koff)[C::KWIN_W], int T, int stage) __attribute__((always_inline)) {
+        if ((T & 1) != cpair) return;
+        const u32x4 rk = tile_rsrc(T);
         unsigned char *st = lds + stage * C::KTILE_B;
         perturb_pause();
 #pragma unroll
@@ -328,6 +386,8 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
             kb[0] = base + 64 * (0 ^ (s >> 2));
             kb[1] = base + 64 * (1 ^ (s >> 2));
         }
+        uint32_t koff[C::KWIN_W];  // this wave's byte offsets of its copies in a tile
+        copy_offsets(koff);
         // Q of the block's 16 rows (B operands), loaded at the start of each
         // pass so that it is live in this role's code only
         bf16x8 qf[C::NKS];
@@ -346,9 +406,20 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
             wide_vk_kreads0(kb[0] + so, kb[1] + so);
         };
         // the score block of tile T (its first K fragment reads issued), masked
-        auto scores = [&](int T, int stage, float (&sv)[4]) __attribute__((always_inline)) {
+        // with Tc >= 0 this wave's share of the copy of tile Tc (into its
+        // stage) goes between the MFMAs
+        auto scores = [&](int T, int stage, float (&sv)[4], int Tc) __attribute__((always_inline)) {
             const uint32_t so = stage * C::KTILE_B;
-            const f32x4 sacc = wide_vk_qk(qf, kb[0] + so, kb[1] + so);
+            f32x4 sacc;
+            if (Tc >= 0) {
+                const u32x4 rk = tile_rsrc(Tc);
+                const uint32_t mb = __builtin_amdgcn_readfirstlane(
+                    lds_addr(lds + (Tc & 3) * C::KTILE_B + cm * 1024));
+                perturb_pause();
+                sacc = wide_vk_qk_copy(qf, kb[0] + so, kb[1] + so, koff, rk, mb);
+            } else {
+                sacc = wide_vk_qk(qf, kb[0] + so, kb[1] + so);
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) sv[i] = sacc[i];
             if (T >= first_masked) {
@@ -375,8 +446,6 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
             l = sum_bf16x2(p23, sum_bf16x2(p01, l));
             *(u32x2 *)(lds + C::POFF + (T & 1) * C::PBUF_B + p_wr) = u32x2{p01, p23};
         };
-        uint32_t koff[C::KWIN_W];
-        copy_offsets(koff);
         auto pass = [&](bool set_m) __attribute__((always_inline)) {
             l = 0.f;
             load_q();
@@ -384,7 +453,7 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
             kreads0(0);
             {
                 float sv[4];
-                scores(0, 0, sv);
+                scores(0, 0, sv, -1);
                 if (set_m) {
                     // reference: the row maximum over tile 0
                     const float mx = combine_halves(block_row_max(sv), true) * a.c;
@@ -396,9 +465,10 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
             for (int T = 0; T + 1 < n_tiles; ++T) {
                 float sv[4];
                 kreads0((T + 1) & 3);
-                scores(T + 1, (T + 1) & 3, sv);
+                // this pair's copy of tile T + 3 rides on the score block
+                const bool copies = T + 3 < n_tiles && ((T + 3) & 1) == cpair;
+                scores(T + 1, (T + 1) & 3, sv, copies ? T + 3 : -1);
                 block_p(T + 1, sv);
-                if (T + 3 < n_tiles) dma_tile(koff, T + 3, (T + 3) & 3);
                 copy_barrier(T + 2);
             }
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no copy outlives the pass
@@ -411,7 +481,7 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
             kreads0(0);
             for (int T = 0; T < n_tiles; ++T) {
                 float sv[4];
-                scores(T, T & 3, sv);
+                scores(T, T & 3, sv, -1);
                 M = fmaxf(M, block_row_max(sv) * a.c);
                 if (T + 3 < n_tiles) dma_tile(koff, T + 3, (T + 3) & 3);
                 copy_barrier(T + 1);
