@@ -533,8 +533,7 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
             return __builtin_bit_cast(bf16x8, __builtin_shufflevector(hv[0], hv[1], 0, 1, 2, 3, 4, 5, 6, 7));
         };
         f32x16 oacc[CBW];
-        // O += P·V of tile T: P from its buffer, V from its stage; the copy
-        // of tile T + 3 goes between the LDS reads and the MFMAs
+        // O += P·V of tile T: P from its buffer, V from its stage
         auto pv_tile = [&](int T) __attribute__((always_inline)) {
             const unsigned char *pb = lds + C::POFF + (T & 1) * C::PBUF_B;
             const uint32_t stage_off = (T & 3) * C::KTILE_B;

@@ -5,6 +5,11 @@ rocprofv3 writes, per run directory, ``*_kernel_stats.csv`` (``--kernel-trace
 them to the figures the benchmark and the design notes use:
 
 * the kernel-trace table (calls, average / min / max duration per kernel);
+* the durations of the named kernel over exactly the bench run's timed
+  steps (its dispatches after the warmup ones, from the per-dispatch
+  trace), as median / min / p90 / average, and the rate at the median from
+  the algorithmic work of one launch, beside the bench line's own figures
+  (``--bench-log``: the file holding the JSON line that run printed);
 * HBM traffic per attention launch: FETCH_SIZE and WRITE_SIZE (KiB per
   dispatch) averaged over the attention dispatches, each scaled by the
   factor that makes the same counter read exactly the known byte count of a
@@ -88,6 +93,53 @@ def traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib, kern
     }
 
 
+def dispatch_ns(run_dir: str, kernel_substr: str):
+    """Durations (ns) of the dispatches whose kernel name contains
+    kernel_substr, in dispatch order, from ``*_kernel_trace.csv``."""
+    path = _one(os.path.join(run_dir, "**", "*kernel_trace.csv"))
+    rows = [r for r in csv.DictReader(open(path)) if kernel_substr in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    return [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows]
+
+
+def bench_line(path: str) -> dict:
+    """The last JSON line a bench.py run printed."""
+    line = None
+    for x in open(path):
+        if x.startswith("{"):
+            line = x
+    if line is None:
+        raise ValueError("no bench line in %s" % path)
+    return json.loads(line)
+
+
+def timed_window(ns, line: dict) -> list[str]:
+    """Statistics of the bench run's timed launches (the dispatches after
+    its warmup ones) and the rate at their median, from the work of one
+    launch that the bench line implies (achieved x its average time)."""
+    w, k = int(line["warmup"]), int(line["steps"])
+    xs = sorted(ns[w:w + k])
+    if len(xs) < k:
+        return ["(the trace holds %d dispatches of the kernel, fewer than warmup %d + steps %d)"
+                % (len(ns), w, k)]
+    r = line["roofline"]
+    unit = r["unit"]
+    work = r["achieved"] * r["kernel_ms_avg"]  # unit x ms per launch
+    med, avg = xs[len(xs) // 2], sum(xs) / len(xs)
+    p90 = xs[min(len(xs) - 1, -(-9 * len(xs) // 10) - 1)]
+    return [
+        "Timed launches: dispatches %d .. %d of the kernel (after %d warmup ones)" % (w + 1, w + k, w),
+        "  median %.0f ns, min %d ns, p90 %d ns, average %.0f ns" % (med, xs[0], p90, avg),
+        "  at the median: %.2f %s; at the average: %.2f %s (algorithmic work per launch)"
+        % (work / (med * 1e-6), unit, work / (avg * 1e-6), unit),
+        "Bench line of this run (HIP events, profiler attached): value %s %s, ms_per_step %s,"
+        % (line["value"], line["unit"], line["ms_per_step"]),
+        "  achieved %s %s (frac %s), kernel_ms median %s min %s p90 %s"
+        % (r["achieved"], unit, r["frac"], r.get("kernel_ms_median"), r.get("kernel_ms_min"),
+           r.get("kernel_ms_p90")),
+    ]
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--workload", required=True)
@@ -102,6 +154,7 @@ def main(argv=None) -> int:
                     help="further --pmc run directories: every counter averaged per dispatch")
     ap.add_argument("--commands", help="text file with the rocprofv3 command lines used")
     ap.add_argument("--kernel-sha", help="source hash the counters were taken on")
+    ap.add_argument("--bench-log", help="output of the traced bench.py run (its JSON line)")
     ap.add_argument("--out", required=True, help="output prefix, e.g. profiles/attn_fwd_C4")
     a = ap.parse_args(argv)
 
@@ -114,6 +167,8 @@ def main(argv=None) -> int:
         lines.append("%-60s %6s %14.0f %14s %14s %8s" % (
             (name[:57] + "...") if len(name) > 60 else name, r["Calls"], float(r["AverageNs"]),
             r["MinNs"], r["MaxNs"], r["Percentage"]))
+    if a.bench_log:
+        lines += [""] + timed_window(dispatch_ns(a.trace, a.kernel), bench_line(a.bench_log))
     with open(a.out + "_kernel_trace.txt", "w") as f:
         f.write("\n".join(lines) + "\n")
 
