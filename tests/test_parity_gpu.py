@@ -108,6 +108,17 @@ WIDE = [
     (1, 2, 1, 32, 96, False, True),
     (1, 2, 1, 64, 200, False, True),
     (1, 3, 1, 333, 333, True, True),
+    # 2 .. 6 key tiles, exact and ragged: the score waves' copy of tile T + 3
+    # rides on the score block only while that tile exists, alternating
+    # between the two copy pairs
+    (1, 2, 1, 32, 33, False, True),
+    (1, 2, 1, 32, 64, False, True),
+    (1, 2, 1, 32, 128, False, True),
+    (1, 2, 1, 32, 129, False, True),
+    (1, 2, 1, 32, 160, False, True),
+    (1, 2, 1, 32, 192, False, True),
+    (1, 2, 1, 129, 129, True, True),
+    (1, 2, 1, 192, 192, True, True),
 ]
 
 
