@@ -11,8 +11,8 @@
 //    16 kh .. 16 kh + 15 and rows 16 rh .. 16 rh + 15 and compute it whole
 //    (Sᵀ = K·Qᵀ, 18 k-steps of v_mfma_f32_16x16x32_bf16, their 16 rows of Q
 //    held in registers), apply the mask and the exponential to it and write
-//    P (bf16) to LDS. They also move the K tiles into LDS (LDS-DMA), after
-//    writing P, in the time they would otherwise wait at the barrier.
+//    P (bf16) to LDS. They also move the K tiles into LDS (LDS-DMA), one
+//    copy after each score MFMA, inside the score block.
 //  * Value waves 4..7 (vw = w - 4), after the barrier that publishes a
 //    tile's P, read all of it and accumulate output columns 128 vw ..
 //    128 vw + 127 for all 32 rows (O = P·V split over the value columns),
@@ -31,9 +31,10 @@
 //    period after tile T's barrier one pair of score waves issues tile T + 3
 //    (the pairs take turns), and the barrier two tiles later waits for it.
 //  * Software pipeline, one barrier per tile: after the barrier that
-//    publishes P of tile T, the score waves read K of tile T + 1, run its
-//    score MFMAs, write its P and issue the copy of tile T + 3; the value
-//    waves read P and Vᵀ of tile T and run its P·V MFMAs.
+//    publishes P of tile T, the score waves read K of tile T + 1 and run its
+//    score MFMAs (the copying pair issuing the copy of tile T + 3 between
+//    them), then write its P; the value waves read P and Vᵀ of tile T and
+//    run its P·V MFMAs.
 //  * K rows are 72 16-byte chunks. Chunk c of row r is stored at
 //    c ^ s(r), s(r) = t ^ 4 (t & 1), t = (r / 2) % 8; with the k-group
 //    order below the 16 lanes served together by a fragment read
@@ -54,7 +55,7 @@ struct WideVkCfg {
     static constexpr int TK = 32;  // keys per tile
     static constexpr int NWAVE = 8;
     static constexpr int NT = 64 * NWAVE;
-    static constexpr int NSW = 4;  // score waves (0..3); the others copy
+    static constexpr int NSW = 4;  // score waves (0..3), which also copy; the others do P·V
     static constexpr int KCH = DQK / 8;  // 16-byte chunks per K row
     static constexpr int KROW_B = 2 * DQK;
     static constexpr int KTILE_B = TK * KROW_B;
@@ -68,7 +69,7 @@ struct WideVkCfg {
     static constexpr int KWIN_W = KTILE_B / 1024 / 2;  // 1 KB copies per copying wave per copied tile
     static constexpr int CBW = DV / 32 / (NWAVE - NSW);            // 32-column blocks of O per value wave
     static_assert(NSW == 4 && NWAVE - NSW == 4, "four score waves (two copy pairs), four value waves");
-    static_assert(KTILE_B % 2048 == 0, "tile pieces must split over a pair of copy waves");
+    static_assert(KTILE_B % 2048 == 0, "tile pieces must split over a pair of copying waves");
     static_assert(NKS == 18, "the score block is written for 18 k-steps");
     static_assert(KCH % 8 == 0, "the swizzle permutes aligned groups of 8 chunks");
     static_assert(CBW == 4 && DV <= DQK, "value columns 128 vw .. 128 vw + 127");
