@@ -1,7 +1,8 @@
 // Probes of the tile layer, one wave each, for the GPU unit tests: the MFMA
 // fragment layout, the cross-half wave reductions, the swizzled K fragment
 // path of Q·Kᵀ, the transposed V fragment path of P·V, and the lane layout of
-// the LDS transpose read, and the shader clock under load. They
+// the LDS transpose read, the shader clock under load, and the sustained
+// MFMA rate of the chip on data that toggles like real operands. They
 // check the primitives the attention kernel is built from, separately from it
 // ("Distilling a 4.5 hour CUDA talk", section 9: unit tests over every
 // load/store/layout/MMA combination).
@@ -133,6 +134,73 @@ __global__ void __launch_bounds__(64) clock_probe(uint64_t *out, uint32_t ticks,
     }
 }
 
+// The sustained dense bf16 MFMA rate of the chip: 8 waves per workgroup (two
+// per SIMD), one workgroup per CU (96 KB of LDS each), every wave issuing
+// `iters` x 16 v_mfma_f32_32x32x16_bf16 back to back. Both operands come from
+// LDS through a ring of eight fragment registers read four MFMAs ahead (A is
+// this MFMA's fragment, B the previous one), and LDS holds hashed bf16 values
+// in [-2, 2), so the operand bits toggle as with real data; constant operands
+// let the chip hold a much higher clock. The whole loop is one assembly
+// statement that ends with every fragment read complete. Each wave stores its
+// shader cycles (s_memtime) and constant-rate ticks (s_memrealtime).
+#define MR_RD(q, o) "ds_read_b128 %[" #q "], %[ad] offset:" #o "\n\t"
+#define MR_MF(c, a, b) "s_waitcnt lgkmcnt(3)\n\tv_mfma_f32_32x32x16_bf16 %[" #c "], %[" #a "], %[" #b "], %[" #c "]\n\t"
+constexpr int kRateLdsBytes = 96 * 1024;
+__global__ void __launch_bounds__(512) mfma_rate_probe(uint64_t *out, uint32_t iters) {
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[kRateLdsBytes];
+    for (int i = threadIdx.x; i < 16384 / 2; i += blockDim.x) {
+        uint32_t x = (uint32_t)i * 2654435761u + 0x9E3779B9u;
+        x ^= x >> 15;
+        x *= 2246822519u;
+        x ^= x >> 13;
+        ((__bf16 *)lds)[i] = (__bf16)((float)(x & 0xffffu) * (1.0f / 16384.0f) - 2.0f);
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    const uint32_t ad = lds_addr(lds) + 16u * (uint32_t)lane;  // fragment reads stay below 16 KB
+    f32x16 c0, c1;
+    for (int r = 0; r < 16; ++r) c0[r] = c1[r] = 0.f;
+    u32x4 q0, q1, q2, q3, q4, q5, q6, q7;
+    uint32_t n;
+    const uint64_t t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+    asm volatile(
+        "s_waitcnt lgkmcnt(0)\n\t"
+        "s_mov_b32 %[n], %[iters]\n\t"
+        MR_RD(q7, 7168) "s_waitcnt lgkmcnt(0)\n\t"
+        MR_RD(q0, 0) MR_RD(q1, 1024) MR_RD(q2, 2048) MR_RD(q3, 3072)
+        ".Lmfma_rate_loop%=:\n\t"
+        MR_MF(c0, q0, q7) MR_RD(q4, 4096) MR_MF(c1, q1, q0) MR_RD(q5, 5120)
+        MR_MF(c0, q2, q1) MR_RD(q6, 6144) MR_MF(c1, q3, q2) MR_RD(q7, 7168)
+        MR_MF(c0, q4, q3) MR_RD(q0, 8192) MR_MF(c1, q5, q4) MR_RD(q1, 9216)
+        MR_MF(c0, q6, q5) MR_RD(q2, 10240) MR_MF(c1, q7, q6) MR_RD(q3, 11264)
+        MR_MF(c0, q0, q7) MR_RD(q4, 12288) MR_MF(c1, q1, q0) MR_RD(q5, 13312)
+        MR_MF(c0, q2, q1) MR_RD(q6, 14336) MR_MF(c1, q3, q2) MR_RD(q7, 15360)
+        MR_MF(c0, q4, q3) MR_RD(q0, 0) MR_MF(c1, q5, q4) MR_RD(q1, 1024)
+        MR_MF(c0, q6, q5) MR_RD(q2, 2048) MR_MF(c1, q7, q6) MR_RD(q3, 3072)
+        "s_sub_u32 %[n], %[n], 1\n\t"
+        "s_cmp_lg_u32 %[n], 0\n\t"
+        "s_cbranch_scc1 .Lmfma_rate_loop%=\n\t"
+        "s_waitcnt lgkmcnt(0)\n\t"
+        "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
+        : [c0] "+v"(c0), [c1] "+v"(c1), [q0] "=&v"(q0), [q1] "=&v"(q1), [q2] "=&v"(q2),
+          [q3] "=&v"(q3), [q4] "=&v"(q4), [q5] "=&v"(q5), [q6] "=&v"(q6), [q7] "=&v"(q7),
+          [n] "=&s"(n)
+        : [iters] "s"(iters), [ad] "v"(ad)
+        : "scc", "memory");
+    const uint64_t t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+    float sink = 0.f;
+    for (int r = 0; r < 16; ++r) sink += c0[r] + c1[r];
+    const int wave = threadIdx.x >> 6;
+    if (lane == 0) {
+        out[2 * (8 * blockIdx.x + wave)] = t1 - t0;
+        out[2 * (8 * blockIdx.x + wave) + 1] = r1 - r0;
+    }
+    // keeps the accumulators live; the sum of finite products is never NaN
+    if (sink != sink) out[0] = 0;
+}
+#undef MR_RD
+#undef MR_MF
+
 }  // namespace
 
 extern "C" {
@@ -179,9 +247,6 @@ int tile_selftest_pv(int d, const void *St, const void *V, void *O, void *stream
     return (int)hipGetLastError();
 }
 
-// offsets: 64 device ints; n: number of 16-bit values in LDS (<= 4096).
-// Returns -1 without launching if n is out of range; the caller checks the
-// offsets against n on the host before the call.
 // n_blocks workgroups of the clock probe; out: 2 * n_blocks uint64 (device)
 int tile_selftest_clock(void *out, int n_blocks, unsigned ticks, unsigned max_iter, void *stream) {
     if (!out || n_blocks < 1 || n_blocks > 65536) return -1;
@@ -198,6 +263,19 @@ int tile_selftest_wallclock_khz(void) {
     return khz;
 }
 
+// n_blocks workgroups of the MFMA rate probe, each wave `iters` x 16 MFMAs;
+// out: 16 * n_blocks uint64 (device): per wave its shader cycles, then its
+// s_memrealtime ticks. Returns -1 without launching on a bad argument.
+int tile_selftest_mfma_rate(void *out, int n_blocks, unsigned iters, void *stream) {
+    if (!out || n_blocks < 1 || n_blocks > 4096 || iters < 1 || iters > 10000000u) return -1;
+    hipLaunchKernelGGL(mfma_rate_probe, dim3(n_blocks), dim3(512), 0, (hipStream_t)stream,
+                       (uint64_t *)out, (uint32_t)iters);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// offsets: 64 device ints; n: number of 16-bit values in LDS (<= 4096).
+// Returns -1 without launching if n is out of range; the caller checks the
+// offsets against n on the host before the call.
 int tile_selftest_tr16(const void *offsets, int n, void *out, void *stream) {
     if (n < 1 || n > 4096) return -1;
     hipLaunchKernelGGL(tr16_probe, dim3(1), dim3(64), 0, (hipStream_t)stream, (const int *)offsets,

@@ -11,11 +11,13 @@ timed region. Prints ONE JSON line.
   roofline    = the kernel's own launch time, from HIP events recorded on the
                 stream the kernel is launched on, against the bf16 dense MFMA
                 peak (256 CUs x 4096 flop/clk x 2.4 GHz = 2516.6 TFLOP/s):
-                `achieved` from the average launch; the median (the survey's
-                primary figure), min and p90 beside it; the shader clock the
+                `achieved` from the average launch; the median (the primary
+                figure), min and p90 beside it; the shader clock the
                 chip held under the same load (an in-kernel probe, untimed,
                 after the timed steps) and the fraction of the MFMA rate at
-                that clock
+                that clock; then the dense bf16 MFMA rate the chip sustains
+                on toggling operands (a probe kernel on every CU, also after
+                the timed steps) and the kernel's fraction of it
   cpu_baseline= the fp64 oracle timed on the host over a bounded row sample;
                 `cores` is the threads it used, `host_cores` and
                 `affinity_cores` what the host has and allows
@@ -281,6 +283,87 @@ def kernel_times(ms, clock, work, unit_scale, peak_at_clock=None):
     return out
 
 
+def mfma_sustained(rounds: int = 1, iters: int = 120000):
+    """The dense bf16 MFMA rate this chip sustains on operands that toggle
+    like real data: a probe kernel with one 8-wave workgroup on each of the
+    256 CUs, every wave issuing iters x 16 v_mfma_f32_32x32x16_bf16 fed from
+    LDS (hashed bf16 values in [-2, 2)), about 80 ms per launch. One untimed
+    launch, then `rounds` timed ones (HIP events); the shader clock from each
+    wave's s_memtime cycles over its s_memrealtime ticks. Returns one dict
+    per timed round, or None if the probe library is not built."""
+    import ctypes
+
+    import torch
+    path = os.path.join(ROOT, "accelerator_programming_amd", "libattn_tile_selftest.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.tile_selftest_mfma_rate.restype = ctypes.c_int
+    lib.tile_selftest_mfma_rate.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_uint,
+                                            ctypes.c_void_p]
+    lib.tile_selftest_wallclock_khz.restype = ctypes.c_int
+    khz = lib.tile_selftest_wallclock_khz()
+    nb = 256
+    out = torch.zeros(nb * 16, dtype=torch.int64, device="cuda")
+    stream = torch.cuda.current_stream()
+    flops = nb * 8 * iters * 16 * 2.0 * 32 * 32 * 16
+    res = []
+    torch.cuda.synchronize()
+    for r in range(rounds + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        if lib.tile_selftest_mfma_rate(out.data_ptr(), nb, iters, stream.cuda_stream) != 0:
+            return None
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if r == 0:
+            continue
+        ms = e0.elapsed_time(e1)
+        o = out.view(-1, 2).cpu().double()
+        mhz = sorted((o[:, 0] / o[:, 1] * khz / 1e3).tolist()) if khz > 0 else [0.0]
+        tf = flops / (ms * 1e-3) / 1e12
+        res.append({"tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                    "clock_mhz_median": round(mhz[len(mhz) // 2], 1), "ms": round(ms, 3),
+                    "mfma_per_wave": iters * 16})
+    return res
+
+
+def sustained_block(achieved: float):
+    """For an MFMA-bound line: the probe's sustained rate on this chip, run
+    after the timed steps, and the kernel's fraction of it."""
+    res = mfma_sustained(rounds=1)
+    if not res:
+        return {}
+    r = res[-1]
+    return {"sustained_mfma": {**r, "achieved_frac": round(achieved / r["tflops"], 4),
+                               "source": "probe kernel: 8 waves on each CU issuing "
+                                         "v_mfma_f32_32x32x16_bf16 from LDS on hashed bf16 "
+                                         "operands (bench.py --mfma-ceiling)"}}
+
+
+def mfma_ceiling_main(rounds: int = 3) -> int:
+    """--mfma-ceiling: the probe alone, `rounds` timed launches."""
+    import torch
+    torch.cuda.set_device(0)
+    res = mfma_sustained(rounds=rounds)
+    if not res:
+        print("bench.py: the MFMA rate probe is not built or did not launch", file=sys.stderr)
+        return 2
+    for i, r in enumerate(res):
+        print("round %d: %.3f ms, %.1f TFLOP/s (%.1f %% of %.1f), shader clock %.0f MHz" % (
+            i + 1, r["ms"], r["tflops"], 100 * r["frac_of_peak"], PEAK_BF16_TFLOPS,
+            r["clock_mhz_median"]), file=sys.stderr, flush=True)
+    best = max(res, key=lambda x: x["tflops"])
+    line = {"metric": "sustained dense bf16 MFMA rate, toggling operands, all CUs",
+            "value": best["tflops"], "unit": "TFLOP/s", "higher_is_better": True,
+            "peak": round(PEAK_BF16_TFLOPS, 1), "frac_of_peak": best["frac_of_peak"],
+            "clock_mhz_median": best["clock_mhz_median"], "rounds": res,
+            "config": {"workload": "MFMA rate probe", "workgroups": 256, "waves_per_simd": 2,
+                       "mfma": "v_mfma_f32_32x32x16_bf16"}}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def cpu_info(threads_used: int) -> dict:
     """Host cores: the count the OS reports and the ones this process may use."""
     return {"cores": threads_used, "host_cores": os.cpu_count(),
@@ -307,6 +390,7 @@ def gemm_main(args, w) -> int:
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (kern_avg_ms * 1e-3) / 1e12
     finite = bool(torch.isfinite(c).all().item())
+    sustained = sustained_block(achieved)
     cpu = None
     if not args.no_cpu_baseline:
         threads = min(16, len(os.sched_getaffinity(0)))
@@ -334,6 +418,7 @@ def gemm_main(args, w) -> int:
                      "traffic": traffic_for_current_kernel(w.name, "tile_gemm_" + args.config,
                                                            gemm_source_sha()),
                      **kernel_times(kern_ms, clock, flops, 1e12, peak_at_clock=True),
+                     **sustained,
                      "kernel": "attn::gemm_bf16_nt_kernel"},
         "cpu_baseline": cpu,
     }
@@ -407,6 +492,10 @@ def main() -> int:
                          "attn_fwd_run_rope (R1 times the standalone RoPE kernel)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="instead of attention: the sustained dense bf16 MFMA rate of this chip "
+                         "on toggling operands (a probe kernel, every CU busy), with the clock "
+                         "it held")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of attention: copy a MIB-MiB buffer 3 times (a reference "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
@@ -429,6 +518,9 @@ def main() -> int:
         print(json.dumps({"copy_calibration_bytes_read": 4 * n, "bytes_written": 4 * n,
                           "launches": 3}), flush=True)
         return 0
+
+    if args.mfma_ceiling:
+        return mfma_ceiling_main()
 
     from accelerator_programming_amd import attn
     from accelerator_programming_amd.inputs import GEMM_WORKLOADS, WORKLOADS, make_inputs
@@ -480,6 +572,7 @@ def main() -> int:
     achieved = flops / (kern_avg_ms * 1e-3) / 1e12
     gbs = w.io_bytes() / (kern_avg_ms * 1e-3) / 1e9  # algorithmic bytes (each tensor once)
     finite = bool(torch.isfinite(o).all().item() and torch.isfinite(lse).all().item())
+    sustained = {} if w.decode else sustained_block(achieved)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -513,6 +606,7 @@ def main() -> int:
                           w.name, "attn_fwd_" + args.config + ("_dropout" if drop_thr else "")
                           + ("_rope" if args.rope else "")),
                       **kernel_times(kern_ms, clock, flops, 1e12, peak_at_clock=True),
+                      **sustained,
                       "kernel": ("attn::rope_bf16_kernel (K) + " if args.rope else "")
                       + kernel_name(w, drop_thr > 0, args.rope > 0)} if not w.decode else
                      {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,

@@ -87,3 +87,21 @@ def test_pv_through_transposed_v_reads(lib, d):
     assert lib.tile_selftest_pv(d, Sd.data_ptr(), Vd.data_ptr(), O.data_ptr(), stream()) == 0
     torch.cuda.synchronize()
     assert torch.equal(O.cpu(), St.t() @ V)
+
+
+def test_mfma_rate_probe_counts_every_wave(lib):
+    # the probe behind `bench.py --mfma-ceiling`: every wave of every
+    # workgroup reports a positive cycle and tick count, cycles at least the
+    # 32 per MFMA the pipe needs, and the host rejects bad arguments
+    lib.tile_selftest_mfma_rate.restype = ctypes.c_int
+    lib.tile_selftest_mfma_rate.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_uint,
+                                            ctypes.c_void_p]
+    nb, iters = 8, 200
+    out = torch.zeros(nb * 16, dtype=torch.int64, device="cuda")
+    assert lib.tile_selftest_mfma_rate(out.data_ptr(), nb, iters, stream()) == 0
+    torch.cuda.synchronize()
+    o = out.view(-1, 2).cpu()
+    assert bool((o[:, 0] >= 32 * 16 * iters).all()) and bool((o[:, 1] > 0).all())
+    assert lib.tile_selftest_mfma_rate(out.data_ptr(), 0, iters, stream()) == -1
+    assert lib.tile_selftest_mfma_rate(out.data_ptr(), nb, 0, stream()) == -1
+    assert lib.tile_selftest_mfma_rate(None, nb, iters, stream()) == -1
