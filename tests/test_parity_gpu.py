@@ -155,6 +155,75 @@ def test_edge_shapes(shape):
     case(w)
 
 
+# Seeded random shapes: every combination the kernels branch on (d, dtype,
+# causal, GQA group size, batch, ragged lengths, larger K scales that move the
+# row maxima away from the first keys, explicit softmax scales), drawn from
+# one fixed generator so that the list is the same on every run. Causal
+# shapes have N_kv = N_q (the only causal form the plan accepts).
+def _random_shapes(n: int, seed: int):
+    import random
+    rng = random.Random(seed)
+    out = []
+    for i in range(n):
+        d = rng.choice([64, 128])
+        dtype = torch.float32 if rng.random() < 0.2 else torch.bfloat16
+        causal = rng.random() < 0.5
+        B = rng.choice([1, 2])
+        Hkv = rng.choice([1, 2, 3])
+        Hq = Hkv * rng.choice([1, 2, 4]) if B * Hkv <= 3 else Hkv
+        Nq = rng.choice([rng.randint(1, 40), rng.randint(41, 300), rng.randint(301, 600)])
+        Nkv = Nq if causal else rng.choice([rng.randint(1, 70), rng.randint(71, 600)])
+        k_mult = rng.choice([1.0, 1.0, 2.0, 3.0])
+        scale = rng.choice([0.0, 0.0, 0.05, 0.25])
+        if dtype == torch.float32:
+            # fp32 inputs (served at d = 64) are rounded to bf16 on load:
+            # keep their logits at the default scale, where that rounding
+            # stays inside the bar
+            d, k_mult, scale = 64, 1.0, 0.0
+        out.append((B, Hq, Hkv, Nq, Nkv, d, causal, dtype == torch.float32, k_mult, scale, 9000 + i))
+    return out
+
+
+RANDOM = _random_shapes(24, 20261203)
+
+
+@pytest.mark.parametrize("shape", RANDOM, ids=lambda s: "B%d_Hq%d_Hkv%d_Nq%d_Nkv%d_d%d_%s_%s_K%g_s%g" % (
+    s[0], s[1], s[2], s[3], s[4], s[5], "causal" if s[6] else "full", "fp32" if s[7] else "bf16",
+    s[8], s[9]))
+def test_seeded_random_shapes(shape):
+    B, Hq, Hkv, Nq, Nkv, d, causal, fp32, k_mult, scale, seed = shape
+    w = Workload("rand", B, Hq, Hkv, Nq, Nkv, d, d, causal,
+                 torch.float32 if fp32 else torch.bfloat16, seed, k_mult=k_mult, scale=scale)
+    case(w)
+
+
+def _random_wide(n: int, seed: int):
+    import random
+    rng = random.Random(seed)
+    out = []
+    for i in range(n):
+        vk = rng.random() < 0.6
+        causal = rng.random() < 0.4
+        Hkv = 1 if vk else rng.choice([1, 2])
+        Hq = Hkv * rng.choice([1, 2, 4])
+        Nq = rng.randint(1, 200)
+        Nkv = Nq if causal else rng.randint(1, 400)
+        out.append((1, Hq, Hkv, Nq, Nkv, causal, vk, rng.choice([1.0, 2.0]), 9100 + i))
+    return out
+
+
+RANDOM_WIDE = _random_wide(6, 20261204)
+
+
+@pytest.mark.parametrize("shape", RANDOM_WIDE, ids=lambda s: "B%d_Hq%d_Hkv%d_Nq%d_Nkv%d_%s_%s_K%g" % (
+    s[0], s[1], s[2], s[3], s[4], "causal" if s[5] else "full", "vk" if s[6] else "v", s[7]))
+def test_seeded_random_wide_shapes(shape):
+    B, Hq, Hkv, Nq, Nkv, causal, vk, k_mult, seed = shape
+    w = Workload("rand_wide", B, Hq, Hkv, Nq, Nkv, 576, 512, causal, torch.bfloat16, seed,
+                 k_mult=k_mult, v_from_k=vk)
+    case(w)
+
+
 def test_fp32_ragged_causal():
     w = Workload("fp32", 1, 2, 1, 190, 190, 64, 64, True, torch.float32, 77)
     case(w)
