@@ -46,7 +46,11 @@
 //    K(T+3) and V(T+2), one LDS-DMA after every fourth MFMA of its two MFMA
 //    chains (the copy engine accepts them at about that pace; a burst would
 //    stall the issuing wave), and waits for them (s_waitcnt vmcnt(0)) at the
-//    end of period T+1. One barrier closes each period. LDS-DMA writes 16
+//    end of period T+1. At d = 64 (half the MFMAs per period) the role-1
+//    waves instead issue every copy, all of them at the start of their
+//    period, during their softmax, and wait for them at its end, so the role-0
+//    waves are never held by the copy issue. One barrier closes each period.
+//    LDS-DMA writes 16
 //    bytes per lane at consecutive addresses, so bank-conflict avoidance is
 //    an XOR swizzle of the 16-byte chunks of a row, applied by choosing which
 //    global chunk each lane fetches ("Distilling a 4.5 hour CUDA talk",
@@ -499,9 +503,14 @@ attn_fwd_kernel(const KernelArgs a) {
         }
         // period T (T < n_live, a tile this wave computes): role 0 runs
         // scores(T), P·V(T-1), softmax(T); role 1 softmax(T), P·V(T),
-        // scores(T+1). Copies by group T % 2: K(T+3) and V(T+2), one LDS-DMA
-        // per four MFMAs of the period's two chains, so that the copy engine
-        // is fed at its own pace instead of stalling a wave on a burst.
+        // scores(T+1). Copies of K(T+3) and V(T+2): at d = 128 by group
+        // T % 2, one LDS-DMA per four MFMAs of the period's two chains, so
+        // that the copy engine is fed at its own pace instead of stalling a
+        // wave on a burst, waited for at the end of period T+1; at d = 64 by
+        // the role-1 waves in every period, all at its start (their softmax
+        // has slack there), waited for at its end (measured: C2 +3-4 %, C4
+        // and C3 -1.6 % with the same scheme).
+        constexpr bool BURST = D == 64;
         auto copy_job = [&](auto PAR, int T, int j, const u32x4 &rk, const u32x4 &rv) __attribute__((always_inline)) {
             constexpr int P = decltype(PAR)::value;
             // window j of K(T+3) (j < DPC), else of V(T+2); no branch on
@@ -519,11 +528,16 @@ attn_fwd_kernel(const KernelArgs a) {
             }
         };
         auto period = [&](auto PAR, int T) __attribute__((always_inline)) {
-            constexpr int P = decltype(PAR)::value;  // T % NS
-            constexpr bool copier = (P & 1) == R;    // T % 2 == R
+            constexpr int P = decltype(PAR)::value;          // T % NS
+            constexpr bool copier = !BURST && (P & 1) == R;  // copies between the MFMAs
             const bool masked = T >= n_plain;
             u32x4 rk = {0, 0, 0, 0}, rv = {0, 0, 0, 0};
             if constexpr (copier && sizeof(TIn) == 2) rk = tile_rsrc(false, T + 3), rv = tile_rsrc(true, T + 2);
+            if constexpr (BURST && R == 1) {
+                if constexpr (sizeof(TIn) == 2) rk = tile_rsrc(false, T + 3), rv = tile_rsrc(true, T + 2);
+#pragma unroll
+                for (int j = 0; j < 2 * DPC; ++j) copy_job(PAR, T, j, rk, rv);
+            }
             // P·V: jobs 0 .. DPC-1; scores: jobs DPC .. 2 DPC-1
             auto pv_hook = [&](int f) __attribute__((always_inline)) {
                 if constexpr (copier)
@@ -562,14 +576,16 @@ attn_fwd_kernel(const KernelArgs a) {
                 // (its stage then holds finite stale data or zeros)
                 scores(snext, IC<(P + 1) % NS>{}, sc_hook);
             }
-            if constexpr (!copier) wait_copies();  // this group's copies of the previous period
+            // at d = 128 the other group's copies of the previous period; at
+            // d = 64 role 1's copies of this one
+            if constexpr (BURST ? R == 1 : !copier) wait_copies();
             lds_barrier();
         };
         // period T >= n_live (causal: no key of the tile is visible to this
         // wave's rows): copy duty only, and role 0's P·V of its last tile
         auto tail_period = [&](auto PAR, int T) __attribute__((always_inline)) {
             constexpr int P = decltype(PAR)::value;
-            constexpr bool copier = (P & 1) == R;
+            constexpr bool copier = BURST ? R == 1 : (P & 1) == R;
             if (R == 0 && T == n_live) pv(pprev, (P + NS - 1) % NS * C::TILE * 2, no_hook);
             if constexpr (copier) {
                 u32x4 rk = {0, 0, 0, 0}, rv = {0, 0, 0, 0};
@@ -577,7 +593,7 @@ attn_fwd_kernel(const KernelArgs a) {
 #pragma unroll
                 for (int j = 0; j < 2 * DPC; ++j) copy_job(PAR, T, j, rk, rv);
             }
-            if constexpr (!copier) wait_copies();
+            if constexpr (BURST ? R == 1 : !copier) wait_copies();
             lds_barrier();
         };
         for (int T = 0; T < n_live; T += NS) {
