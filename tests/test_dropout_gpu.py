@@ -63,6 +63,33 @@ def test_dropout_parity(case):
     check(o, lse, q, k, v, causal, w.softmax_scale, int(p * 256), seed)
 
 
+def _random_drop(n: int, seed: int):
+    import random
+    rng = random.Random(seed)
+    out = []
+    for i in range(n):
+        d = rng.choice([64, 128])
+        Hkv = rng.choice([1, 2])
+        Hq = Hkv * rng.choice([1, 2, 4])
+        N = rng.randint(1, 400)
+        out.append((rng.choice([1, 2]), Hq, Hkv, N, d, rng.random() < 0.5, torch.bfloat16,
+                    rng.choice([1, 26, 64, 128, 200]) / 256.0, rng.randrange(1 << 48)))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_drop(8, 20261206),
+                         ids=lambda c: "B%d_Hq%d_Hkv%d_N%d_d%d_%s_p%g" % (c[0], c[1], c[2], c[3], c[4],
+                                                                       "causal" if c[5] else "full", c[7]))
+def test_dropout_seeded_random_shapes(case):
+    # drawn from one fixed generator: d, causal, GQA group, ragged lengths,
+    # drop probabilities across the 1/256 steps and 48-bit seeds
+    B, Hq, Hkv, N, d, causal, dtype, p, seed = case
+    w = Workload("drop_rand", B, Hq, Hkv, N, N, d, d, causal, dtype, 9300 + N)
+    q, k, v = make_inputs(w, "cuda")
+    o, lse = run_drop(q, k, v, causal, w.softmax_scale, p, seed)
+    check(o, lse, q, k, v, causal, w.softmax_scale, int(p * 256), seed)
+
+
 def test_dropout_full_size_sampled_rows():
     q, k, v = make_inputs(C3, "cuda")
     o, lse = run_drop(q, k, v, True, C3.softmax_scale, 0.1, 2024)

@@ -326,6 +326,33 @@ def test_split_kv_shapes(shape):
     compare(o, lse, q, k, v, False, w.softmax_scale)
 
 
+def _random_split(n: int, seed: int):
+    import random
+    rng = random.Random(seed)
+    out = []
+    for i in range(n):
+        d = rng.choice([64, 128])
+        Hkv = rng.choice([1, 2, 4])
+        group = rng.choice([1, 2, 4, 8])
+        Nq = rng.randint(1, max(1, 64 // group))  # group * N_q <= 64
+        Nkv = rng.choice([rng.randint(1, 200), rng.randint(201, 3000)])
+        ns = rng.choice([0, 0, 1, 3, 7, 16])
+        out.append((rng.choice([1, 2]), Hkv * group, Hkv, Nq, Nkv, d, ns))
+    return out
+
+
+RANDOM_SPLIT = _random_split(10, 20261205)
+
+
+@pytest.mark.parametrize("shape", RANDOM_SPLIT, ids=lambda s: "B%d_Hq%d_Hkv%d_Nq%d_Nkv%d_d%d_s%d" % s)
+def test_seeded_random_split_kv_shapes(shape):
+    B, Hq, Hkv, Nq, Nkv, d, ns = shape
+    w = Workload("rand_split", B, Hq, Hkv, Nq, Nkv, d, d, False, torch.bfloat16, 9200 + Nkv)
+    q, k, v = make_inputs(w, "cuda")
+    o, lse = run_split(q, k, v, w.softmax_scale, ns)
+    compare(o, lse, q, k, v, False, w.softmax_scale)
+
+
 def test_split_kv_equals_single_pass_within_tolerance():
     w = Workload("split_vs_full", 1, 8, 2, 8, 2048, 128, 128, False, torch.bfloat16, 4242)
     q, k, v = make_inputs(w, "cuda")

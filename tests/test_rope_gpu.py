@@ -97,6 +97,25 @@ def test_rope_attention_parity(B, Hq, Hkv, N, d, causal, base):
     check_attention(o, lse, q, k, v, causal, w.softmax_scale, base)
 
 
+def _random_rope(n: int, seed: int):
+    import random
+    rng = random.Random(seed)
+    out = []
+    for i in range(n):
+        Hkv = rng.choice([1, 2])
+        out.append((rng.choice([1, 2]), Hkv * rng.choice([1, 2, 4]), Hkv, rng.randint(1, 400),
+                    rng.choice([64, 128]), rng.random() < 0.5, rng.choice([100.0, 10000.0, 500000.0])))
+    return out
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,causal,base", _random_rope(6, 20261207))
+def test_rope_attention_seeded_random_shapes(B, Hq, Hkv, N, d, causal, base):
+    w = Workload("rope_rand", B, Hq, Hkv, N, N, d, d, causal, torch.bfloat16, 9400 + N)
+    q, k, v = make_inputs(w, "cuda")
+    o, lse = run_rope_attention(q, k, v, causal, w.softmax_scale, base)
+    check_attention(o, lse, q, k, v, causal, w.softmax_scale, base)
+
+
 def test_rope_attention_full_size_sampled_rows():
     q, k, v = make_inputs(C4, "cuda")
     o, lse = run_rope_attention(q, k, v, True, C4.softmax_scale, 500000.0)
