@@ -13,6 +13,7 @@
 #include "attn_fwd_kernel.hpp"
 #include "attn_fwd_wide_kernel.hpp"
 #include "attn_fwd_wide_vk_kernel.hpp"
+#include "attn_fwd_wide_vk_split_kernel.hpp"
 #include "attn_split_kernel.hpp"
 
 using attn::KernelArgs;
@@ -197,21 +198,43 @@ KernelArgs make_args(const attn_fwd_plan *plan, const void *Q, const void *K, co
 // ---- split-KV path (few query rows per kv head, non-causal) ----------------
 constexpr int32_t kMaxSplits = 64;  // the merge holds one split per lane
 
+using WVS = attn::WideVkSplitCfg<576, 512>;
+
+// wide heads (d_qk 576, d_v 512) with V inside K: 64-row tiles of each
+// (batch, head) over key ranges (the V-in-K check needs the pointers and is
+// made at run time)
+bool wide_split(const attn_fwd_plan *pl) { return pl->variant == V_D576_BF16; }
+
 bool split_supported(const attn_fwd_plan *pl) {
     const attn_fwd_params &p = pl->p;
+    if (p.causal) return false;
+    if (wide_split(pl)) {
+        // one 512-thread workgroup per (range, batch, head, 64-row tile): at
+        // the most ranges the launch stays below 2^32 work-items
+        const int64_t items = p.B * p.H_q * ((p.N + WVS::TQ - 1) / WVS::TQ);
+        return items * kMaxSplits * WVS::NT < ((int64_t)1 << 32);
+    }
     // one 256-thread workgroup per (split, batch, kv head) and one per merged
     // row (at most 64 per (batch, kv head)): each launch stays below 2^32
     // work-items
-    return (pl->variant == V_D64_BF16 || pl->variant == V_D128_BF16) && !p.causal &&
+    return (pl->variant == V_D64_BF16 || pl->variant == V_D128_BF16) &&
            (p.H_q / p.H_kv) * p.N <= attn::SplitCfg<64>::ROWS && (int64_t)p.B * p.H_kv <= (1 << 18);
 }
 
-// about two workgroups per CU (256 CUs), at least one 64-key tile per split
+// about two workgroups per CU (256 CUs), at least one 64-key tile per split;
+// wide heads: about one 512-thread workgroup per CU, at least one 32-key tile
 int32_t auto_splits(const attn_fwd_plan *pl) {
     const attn_fwd_params &p = pl->p;
-    const int64_t groups = p.B * p.H_kv;
-    const int64_t tiles = (p.N_kv + 63) / 64;
-    int64_t n = (512 + groups - 1) / groups;
+    int64_t n, tiles;
+    if (wide_split(pl)) {
+        const int64_t items = p.B * p.H_q * ((p.N + WVS::TQ - 1) / WVS::TQ);
+        tiles = (p.N_kv + WVS::TK - 1) / WVS::TK;
+        n = (256 + items - 1) / items;
+    } else {
+        const int64_t groups = p.B * p.H_kv;
+        tiles = (p.N_kv + 63) / 64;
+        n = (512 + groups - 1) / groups;
+    }
     if (n > tiles) n = tiles;
     if (n > kMaxSplits) n = kMaxSplits;
     return (int32_t)(n < 1 ? 1 : n);
@@ -243,6 +266,30 @@ hipError_t launch_split(const attn_fwd_plan *pl, const KernelArgs &a, int32_t n,
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((attn::attn_split_merge<D>), dim3((uint32_t)rows), dim3(256), 0, stream,
+                       (const float *)sa.opart, (const float *)sa.lpart, n, rows, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_wide_split(const attn_fwd_plan *pl, KernelArgs a, int32_t n, float *ws, hipStream_t stream) {
+    const attn_fwd_params &p = pl->p;
+    const int64_t rows = p.B * p.H_q * p.N;
+    a.n_qtiles = (int32_t)((p.N + WVS::TQ - 1) / WVS::TQ);
+    attn::SplitArgs sa;
+    sa.a = a;
+    sa.opart = ws;
+    sa.lpart = ws + (int64_t)n * rows * 512;
+    sa.n_splits = n;
+    const int64_t tiles = (p.N_kv + WVS::TK - 1) / WVS::TK;
+    sa.split_len = (int32_t)(((tiles + n - 1) / n) * WVS::TK);
+    sa.rows = 0;
+    const int64_t grid = (int64_t)n * p.B * p.H_q * a.n_qtiles;
+    hipLaunchKernelGGL((attn::attn_fwd_wide_vk_split_kernel<576, 512>), dim3((uint32_t)grid), dim3(WVS::NT), 0,
+                       stream, sa);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t items = rows * (512 / 4);
+    const int64_t mgrid = items / 256 < 2048 ? (items + 255) / 256 : 2048;
+    hipLaunchKernelGGL((attn::attn_split_merge_wide<512>), dim3((uint32_t)mgrid), dim3(256), 0, stream,
                        (const float *)sa.opart, (const float *)sa.lpart, n, rows, a);
     return hipGetLastError();
 }
@@ -480,9 +527,11 @@ attn_status attn_fwd_run_split(const attn_fwd_plan *plan, const void *Q, const v
     if (n_splits > kMaxSplits) return ATTN_ERR_INVALID;
     if (workspace_bytes < split_workspace(plan, n_splits)) return ATTN_ERR_INVALID;
     const KernelArgs a = make_args(plan, Q, K, V, O, lse);
+    if (wide_split(plan) && !a.v_in_k) return ATTN_ERR_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
-    const hipError_t e = plan->variant == V_D128_BF16 ? launch_split<128>(plan, a, n_splits, (float *)workspace, s)
-                                                      : launch_split<64>(plan, a, n_splits, (float *)workspace, s);
+    const hipError_t e = wide_split(plan) ? launch_wide_split(plan, a, n_splits, (float *)workspace, s)
+                         : plan->variant == V_D128_BF16 ? launch_split<128>(plan, a, n_splits, (float *)workspace, s)
+                                                        : launch_split<64>(plan, a, n_splits, (float *)workspace, s);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
@@ -499,12 +548,14 @@ attn_status attn_fwd_run_split_noalloc(const attn_fwd_plan *plan, const void *Q,
     if (n_splits > kMaxSplits) return ATTN_ERR_INVALID;
     const int64_t need = split_workspace(plan, n_splits);
     if (need > ATTN_SPLIT_SCRATCH_BYTES) return ATTN_ERR_TOO_LARGE;
+    const KernelArgs a = make_args(plan, Q, K, V, O, lse);
+    if (wide_split(plan) && !a.v_in_k) return ATTN_ERR_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
     void *ws = nullptr;
     if (scratch_address(s, &ws) != hipSuccess) return ATTN_ERR_HIP;
-    const KernelArgs a = make_args(plan, Q, K, V, O, lse);
-    const hipError_t e = plan->variant == V_D128_BF16 ? launch_split<128>(plan, a, n_splits, (float *)ws, s)
-                                                      : launch_split<64>(plan, a, n_splits, (float *)ws, s);
+    const hipError_t e = wide_split(plan) ? launch_wide_split(plan, a, n_splits, (float *)ws, s)
+                         : plan->variant == V_D128_BF16 ? launch_split<128>(plan, a, n_splits, (float *)ws, s)
+                                                        : launch_split<64>(plan, a, n_splits, (float *)ws, s);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

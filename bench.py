@@ -42,17 +42,19 @@ METRIC = "attention fwd TFLOP/s on 1 MI355X + % of bf16 MFMA peak (causal FLOPs 
 DROPOUT_SEED = 1234
 
 
-def kernel_source_sha(split: bool = False) -> str:
+def kernel_source_sha(split: bool = False, wide_split: bool = False) -> str:
     """Hash of the sources an attention profile was taken on: the host code,
-    the tile layer and RoPE, plus the main and wide kernels, or, for the
-    split-KV path, its own kernel and the main kernel header it includes."""
+    the tile layer and RoPE, plus the main and wide kernels (wide_split: and
+    the split-KV header the wide split kernel includes), or, for the d 64 /
+    128 split-KV path, its own kernel and the main kernel header it includes."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "accelerator_programming_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
         if split:
             take = name in ("attn_fwd.hip", "attn_fwd_kernel.hpp", "attn_split_kernel.hpp", "tile.hpp", "rope.hpp")
         else:
-            take = name.startswith("attn_fwd") or name in ("tile.hpp", "rope.hpp")
+            take = name.startswith("attn_fwd") or name in ("tile.hpp", "rope.hpp") or (
+                wide_split and name == "attn_split_kernel.hpp")
         if take:
             with open(os.path.join(csrc, name), "rb") as f:
                 h.update(name.encode() + b"\0" + f.read())
@@ -68,11 +70,20 @@ def gemm_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def kernel_name(w, dropout=False, rope=False):
+def wide_split_path(w, single_pass=False) -> bool:
+    """Wide heads with V inside K, not causal: timed through the split-KV
+    entry point (64-row tiles over key ranges, then the merge) unless
+    single_pass asks for attn_fwd_run."""
+    return w.dqk == 576 and w.v_from_k and not w.causal and not w.decode and not single_pass
+
+
+def kernel_name(w, dropout=False, rope=False, single_pass=False):
     """The kernel the library launches for workload w (as rocprofv3 names it)."""
     causal = "true" if w.causal else "false"
     if w.decode:
         return "attn::attn_split_kernel<%d> + attn::attn_split_merge<%d>" % (w.dqk, w.dqk)
+    if wide_split_path(w, single_pass):
+        return "attn::attn_fwd_wide_vk_split_kernel<576, 512> + attn::attn_split_merge_wide<512>"
     if w.dqk == 576:
         # V given as the leading columns of K takes the kernel that stages K only
         return "attn::attn_fwd_wide_%skernel<576, 512, %s>" % ("vk_" if w.v_from_k else "", causal)
@@ -490,6 +501,9 @@ def main() -> int:
     ap.add_argument("--rope", type=float, default=0.0, metavar="BASE",
                     help="attention workloads: RoPE(Q), RoPE(K) with this base through "
                          "attn_fwd_run_rope (R1 times the standalone RoPE kernel)")
+    ap.add_argument("--single-pass", action="store_true",
+                    help="wide heads with V inside K (C5): time attn_fwd_run instead of the "
+                         "split-KV entry point")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--mfma-ceiling", action="store_true",
@@ -536,7 +550,7 @@ def main() -> int:
     o = torch.empty((B, Hq, N, w.dv), dtype=q.dtype, device="cuda")
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device="cuda")
     op = attn.AttnFwd(q, k, v, w.causal, w.softmax_scale, o)
-    if w.decode:
+    if w.decode or wide_split_path(w, args.single_pass):
         # split-KV path; its workspace is allocated here, outside the timed steps
         ws = torch.empty(attn.attn_fwd_split_workspace_bytes(op.plan, 0), dtype=torch.uint8,
                          device="cuda")
@@ -604,11 +618,12 @@ def main() -> int:
                       "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                       "traffic": traffic_for_current_kernel(
                           w.name, "attn_fwd_" + args.config + ("_dropout" if drop_thr else "")
-                          + ("_rope" if args.rope else "")),
+                          + ("_rope" if args.rope else "") + ("_single_pass" if args.single_pass else ""),
+                          kernel_source_sha(wide_split=wide_split_path(w, args.single_pass))),
                       **kernel_times(kern_ms, clock, flops, 1e12, peak_at_clock=True),
                       **sustained,
                       "kernel": ("attn::rope_bf16_kernel (K) + " if args.rope else "")
-                      + kernel_name(w, drop_thr > 0, args.rope > 0)} if not w.decode else
+                      + kernel_name(w, drop_thr > 0, args.rope > 0, args.single_pass)} if not w.decode else
                      {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                       "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                       "traffic": traffic_for_current_kernel(w.name, "attn_split_" + args.config,

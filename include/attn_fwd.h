@@ -176,16 +176,26 @@ attn_status attn_fwd_run_rope(const attn_fwd_plan *plan, const void *Q, const vo
  * O = Σ_s exp(lse_s - lse) O_s. The result equals attn_fwd_run's (same
  * method, "Distilling a 4.5 hour CUDA talk", section 7: the running max and
  * normalizer carried across key tiles, here also across ranges).
- * Served problems: the plan's (d, d_v, dtype) is (64, 64, bf16) or
- * (128, 128, bf16), not causal, (H_q / H_kv) * N <= 64 (all query rows
- * of a kv head fit one workgroup) and B * H_kv <= 2^18 (the launches'
- * work-items fit 32 bits).
+ * Served problems, never causal:
+ *   - (d, d_v, dtype) (64, 64, bf16) or (128, 128, bf16) with
+ *     (H_q / H_kv) * N <= 64 (all query rows of a kv head fit one
+ *     workgroup) and B * H_kv <= 2^18 (the launches' work-items fit 32 bits);
+ *   - (576, 512, bf16), wide heads whose V is the first 512 columns of K
+ *     (V == K with K's strides: the kernel reads V from the K tiles it
+ *     copies), any N: each workgroup takes 64 query rows of one (batch,
+ *     head) over one key range, with B * H_q * ceil(N / 64) < 2^17 (the
+ *     launch's work-items fit 32 bits at 64 ranges).
+ *     Whether V lies inside K is known only from the pointers, so
+ *     attn_fwd_split_count serves such plans and the run entry points return
+ *     ATTN_ERR_UNSUPPORTED, before any HIP call, for a V of its own
+ *     (attn_fwd_run serves that).
  */
 
 /*
  * attn_fwd_split_count - the number of key ranges the library would use for
- * the plan (enough workgroups for every CU, at most 64, at least one 64-key
- * tile each), or 0 if the split path does not serve the plan (or plan is NULL).
+ * the plan (enough workgroups for every CU, at most 64, at least one key tile
+ * each: 64 keys, 32 for wide heads), or 0 if the split path does not serve
+ * the plan (or plan is NULL).
  */
 int32_t attn_fwd_split_count(const attn_fwd_plan *plan);
 
@@ -205,7 +215,8 @@ int64_t attn_fwd_split_workspace_bytes(const attn_fwd_plan *plan, int32_t n_spli
  * scratch. Two kernels are queued on `stream`; calls that share a workspace
  * must not overlap. Returns ATTN_ERR_INVALID for NULL or misaligned pointers,
  * n_splits > 64 or a short workspace; ATTN_ERR_UNSUPPORTED if the split path
- * does not serve the plan; ATTN_ERR_HIP if a launch fails.
+ * does not serve the plan or (wide heads) V is not inside K; ATTN_ERR_HIP if
+ * a launch fails.
  */
 attn_status attn_fwd_run_split(const attn_fwd_plan *plan, const void *Q, const void *K,
                                const void *V, void *O, float *lse, int32_t n_splits,

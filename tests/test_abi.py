@@ -214,9 +214,11 @@ def test_split_count_and_workspace_size():
 @pytest.mark.parametrize("kw", [
     dict(causal=1, N=4096),                      # causal
     dict(N=32),                                  # 4 x 32 = 128 query rows per kv head
-    dict(d=576, d_v=512, H_q=128, H_kv=1, N=1),  # wide heads
+    dict(d=576, d_v=512, H_q=128, H_kv=1, N=64, N_kv=64, causal=1),  # wide heads, causal
     dict(B=1 << 16, H_q=32, H_kv=8, N=1),         # 2^19 (batch, kv head) pairs
-], ids=["causal", "too_many_rows", "wide", "too_many_groups"])
+    dict(d=64, d_v=64, dtype=1),                  # fp32
+    dict(d=576, d_v=512, B=1024, H_q=128, H_kv=1, N=64, N_kv=64),  # 2^17 wide row tiles
+], ids=["causal", "too_many_rows", "wide_causal", "too_many_groups", "fp32", "wide_too_many_tiles"])
 def test_split_path_declines_unserved_plans(kw):
     plan = split_plan(**kw)
     try:
@@ -225,6 +227,63 @@ def test_split_path_declines_unserved_plans(kw):
         L = attn.lib()
         assert L.attn_fwd_run_split(plan, 16, 16, 16, 16, None, 0, 16, 1 << 30, None) == \
             ATTN_ERR_UNSUPPORTED
+    finally:
+        attn.attn_fwd_destroy(plan)
+
+
+def wide_split_plan(**kw):
+    args = dict(B=1, H_q=128, H_kv=1, N=64, N_kv=8192, d=576, d_v=512, causal=0,
+                scale=1 / math.sqrt(192))
+    args.update(kw)
+    return attn.attn_fwd_create_ex(ex_params(**args))
+
+
+def test_wide_split_count_and_workspace_size():
+    # 64-row tiles of each (batch, head): 128 of them at 64 rows per head, so
+    # two ranges give one workgroup per CU; at least one 32-key tile per range
+    plan = wide_split_plan()
+    try:
+        rows = 128 * 64
+        assert attn.attn_fwd_split_count(plan) == 2
+        assert attn.attn_fwd_split_workspace_bytes(plan, 0) == 2 * rows * (512 + 1) * 4
+        assert attn.attn_fwd_split_workspace_bytes(plan, 7) == 7 * rows * (512 + 1) * 4
+        assert attn.attn_fwd_split_workspace_bytes(plan, 65) == -1
+    finally:
+        attn.attn_fwd_destroy(plan)
+    for kw, n in [(dict(H_q=1, N=1, N_kv=40), 2),       # two 32-key tiles
+                  (dict(H_q=4, N=65, N_kv=8192), 32),  # 8 row tiles
+                  (dict(H_q=1, N=1, N_kv=1 << 20), 64)]:  # the cap
+        plan = wide_split_plan(**kw)
+        try:
+            assert attn.attn_fwd_split_count(plan) == n, kw
+        finally:
+            attn.attn_fwd_destroy(plan)
+
+
+def test_wide_split_refuses_a_separate_v_before_launch():
+    # the wide split kernel reads V from the copied K tiles: V must be the
+    # first 512 columns of K (same pointer and strides); anything else is
+    # refused before any HIP call (a problem small enough for the static
+    # scratch, so noalloc reaches that check)
+    plan = wide_split_plan(H_q=2, N=8, N_kv=256)
+    try:
+        L = attn.lib()
+        need = attn.attn_fwd_split_workspace_bytes(plan, 0)
+        assert L.attn_fwd_run_split(plan, 16, 16, 32, 16, None, 0, 16, need, None) == \
+            ATTN_ERR_UNSUPPORTED
+        assert L.attn_fwd_run_split_noalloc(plan, 16, 16, 32, 16, None, 0, None) == \
+            ATTN_ERR_UNSUPPORTED
+    finally:
+        attn.attn_fwd_destroy(plan)
+
+
+def test_wide_split_at_full_size_exceeds_the_static_scratch():
+    # 2 ranges x 8192 rows x 513 floats = 33.6 MB > 16 MiB
+    from accelerator_programming_amd.attn import ATTN_ERR_TOO_LARGE
+    plan = wide_split_plan()
+    try:
+        assert attn.lib().attn_fwd_run_split_noalloc(plan, 16, 16, 16, 16, None, 0, None) == \
+            ATTN_ERR_TOO_LARGE
     finally:
         attn.attn_fwd_destroy(plan)
 

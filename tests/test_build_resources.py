@@ -24,6 +24,7 @@ LIBS = ["libattn_fwd.so", "libattn_fwd_perturb.so", "libattn_tile_selftest.so"]
 # kernel name fragment -> (threads per workgroup, workgroups per CU it is
 # designed for); the first fragment that matches a kernel's name applies
 BUDGET = [
+    ("attn_fwd_wide_vk_split_kernel", 512, 1),
     ("attn_fwd_wide_vk_kernel", 512, 1),
     ("attn_fwd_wide_kernel", 256, 1),
     ("attn_fwd_kernel", 512, 1),

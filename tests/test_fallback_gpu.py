@@ -235,3 +235,17 @@ def test_split_path_with_an_outlier_key():
     o, lse = run(q, k, v, False, w.softmax_scale, "split")
     Oref, Lref, _ = oracle.attention_fp64(q, k, v, False, w.softmax_scale)
     compare(o, lse, Oref, Lref)
+
+
+def test_wide_split_path_with_outlier_keys():
+    # the wide split kernel takes each range's own first 32-key tile as the
+    # rows' reference: outliers past that tile, in either range (keys 0 .. 255
+    # and 256 .. 499 at two ranges), send the range's workgroup through the
+    # exact pass; the gaps checked in make() are against the row's first 32
+    # keys, and the other tiles' scores are drawn alike
+    w = Workload("fbws", 1, 3, 1, 64, 500, 576, 512, False, torch.bfloat16, 917, v_from_k=True)
+    plants = [(0, 1, 5, 300, 8.0, "over"), (0, 2, 63, 100, 8.0, "over"), (0, 0, 30, 480, 2.0, "mid")]
+    q, k, v = make(w, plants)
+    o, lse = run(q, k, v, False, w.softmax_scale, "split", n_splits=2)
+    Oref, Lref, _ = oracle.attention_fp64(q, k, v, False, w.softmax_scale)
+    compare(o, lse, Oref, Lref)

@@ -372,6 +372,91 @@ def test_decode_workloads_full_size_sampled(name):
     compare(o, lse, q, k, v, False, w.softmax_scale, rows=sample_rows(w, 128))
 
 
+# wide heads with V inside K (d_qk 576, d_v 512, V the first 512 columns of
+# K): 64 query rows of one head per workgroup over 32-key tiles of one range
+WIDE_SPLIT = [
+    # B, Hq, Hkv, Nq, Nkv, n_splits (0: the library's count)
+    (1, 4, 1, 64, 1000, 0),    # one full row tile, one 32-key tile per range
+    (1, 2, 1, 17, 333, 3),     # ragged rows, ragged last range and tile
+    (2, 3, 1, 130, 257, 5),    # three row tiles; the last range holds one key
+    (1, 2, 1, 8, 100, 8),      # more ranges than tiles: empty ranges
+    (1, 4, 2, 40, 200, 2),     # two kv heads
+    (1, 2, 1, 1, 64, 1),       # one row, one range
+    (1, 2, 1, 64, 4096, 64),   # the most ranges, two tiles each
+    (1, 2, 1, 50, 700, 3),     # 8, 8 and 6 tiles: copies three tiles ahead in each range
+    (1, 1, 1, 3, 33, 0),       # library count over two tiles, the second one key
+]
+
+
+@pytest.mark.parametrize("shape", WIDE_SPLIT, ids=lambda s: "B%d_Hq%d_Hkv%d_Nq%d_Nkv%d_s%d" % s)
+def test_wide_split_kv_shapes(shape):
+    B, Hq, Hkv, Nq, Nkv, ns = shape
+    w = Workload("wsplit", B, Hq, Hkv, Nq, Nkv, 576, 512, False, torch.bfloat16, 500 + Nkv + Nq,
+                 v_from_k=True)
+    q, k, v = make_inputs(w, "cuda")
+    o, lse = run_split(q, k, v, w.softmax_scale, ns)
+    compare(o, lse, q, k, v, False, w.softmax_scale)
+
+
+def _random_wide_split(n: int, seed: int):
+    import random
+    rng = random.Random(seed)
+    out = []
+    for i in range(n):
+        Hkv = rng.choice([1, 1, 2])
+        Hq = Hkv * rng.choice([1, 2, 3])
+        Nq = rng.choice([rng.randint(1, 64), rng.randint(65, 150)])
+        Nkv = rng.choice([rng.randint(1, 100), rng.randint(101, 1500)])
+        ns = rng.choice([0, 0, 1, 2, 3, 5, 9])
+        out.append((1, Hq, Hkv, Nq, Nkv, ns, rng.choice([1.0, 2.0]), 9400 + i))
+    return out
+
+
+RANDOM_WIDE_SPLIT = _random_wide_split(6, 20261208)
+
+
+@pytest.mark.parametrize("shape", RANDOM_WIDE_SPLIT,
+                         ids=lambda s: "B%d_Hq%d_Hkv%d_Nq%d_Nkv%d_s%d_k%g_seed%d" % s)
+def test_seeded_random_wide_split_kv_shapes(shape):
+    B, Hq, Hkv, Nq, Nkv, ns, k_mult, seed = shape
+    w = Workload("rand_wsplit", B, Hq, Hkv, Nq, Nkv, 576, 512, False, torch.bfloat16, seed,
+                 k_mult=k_mult, v_from_k=True)
+    q, k, v = make_inputs(w, "cuda")
+    o, lse = run_split(q, k, v, w.softmax_scale, ns)
+    compare(o, lse, q, k, v, False, w.softmax_scale)
+
+
+def test_c5_split_full_size_sampled():
+    q, k, v = make_inputs(C5, "cuda")
+    o, lse = run_split(q, k, v, C5.softmax_scale, 0)
+    compare(o, lse, q, k, v, False, C5.softmax_scale, rows=sample_rows(C5, 256))
+
+
+def test_wide_split_equals_single_pass_within_tolerance():
+    w = C5.with_(Hq=8, Nkv=3000)
+    q, k, v = make_inputs(w, "cuda")
+    o1, l1 = run_split(q, k, v, w.softmax_scale, 0)
+    o2, l2 = run_gpu(q, k, v, False, w.softmax_scale)
+    torch.cuda.synchronize()
+    assert (o1.float() - o2.float()).abs().max().item() <= TOL_O
+    assert (l1 - l2).abs().max().item() <= TOL_LSE
+
+
+def test_wide_split_needs_v_inside_k():
+    # the wide split kernel reads V from the K tiles it copies: a V of its
+    # own is refused at run time (attn_fwd_run serves it)
+    w = Workload("wsplit_v", 1, 2, 1, 8, 100, 576, 512, False, torch.bfloat16, 77)
+    q, k, v = make_inputs(w, "cuda")
+    o = torch.empty((1, 2, 8, 512), dtype=torch.bfloat16, device="cuda")
+    op = attn.AttnFwd(q, k, v, False, w.softmax_scale, o)
+    try:
+        assert op.split_count() >= 1
+        with pytest.raises(attn.AttnError):
+            op.run_split(q, k, v, o)
+    finally:
+        op.close()
+
+
 def test_binding_rejects_tensors_that_do_not_match_the_plan():
     # the kernels index memory from the plan: a smaller or differently laid
     # out tensor is refused in the binding, before any launch

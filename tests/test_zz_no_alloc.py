@@ -18,8 +18,12 @@ from accelerator_programming_amd.inputs import Workload, make_inputs
 pytestmark = pytest.mark.gpu
 
 
+def out_like(q, v):
+    return torch.empty(q.shape[:3] + v.shape[3:], dtype=q.dtype, device=q.device)
+
+
 def via_workspace(q, k, v, scale, n_splits):
-    o = torch.empty_like(q)
+    o = out_like(q, v)
     lse = torch.empty(q.shape[:3], device=q.device)
     op = attn.AttnFwd(q, k, v, False, scale, o)
     try:
@@ -31,7 +35,7 @@ def via_workspace(q, k, v, scale, n_splits):
 
 def via_static_scratch(q, k, v, scale, n_splits):
     # straight through the C entry point; the plan is the only host object
-    o = torch.empty_like(q)
+    o = out_like(q, v)
     lse = torch.empty(q.shape[:3], device=q.device)
     params = attn.params_for(q, k, v, False, scale, o)
     plan = attn.attn_fwd_create_ex(params)
@@ -45,13 +49,7 @@ def via_static_scratch(q, k, v, scale, n_splits):
     return o, lse
 
 
-def test_noalloc_matches_workspace_entry_point_twice():
-    shapes = [
-        # the larger problem first (its partials fill more of the buffer),
-        # then a smaller one that reuses the same buffer
-        (Workload("na1", 4, 32, 8, 1, 8192, 128, 128, False, torch.bfloat16, 4101), 0),
-        (Workload("na2", 1, 8, 2, 3, 1000, 64, 64, False, torch.bfloat16, 4102), 5),
-    ]
+def check_twice(shapes):
     for w, ns in shapes:
         q, k, v = make_inputs(w, "cuda")
         print("noalloc case", w.name, "n_splits", ns, flush=True)
@@ -62,3 +60,21 @@ def test_noalloc_matches_workspace_entry_point_twice():
         Oref, Lref, _ = oracle.attention_fp64(q, k, v, False, w.softmax_scale)
         assert np.abs(o1.float().cpu().numpy() - Oref).max() <= 2e-2
         assert np.abs(l1.cpu().numpy() - Lref).max() <= 1e-2
+
+
+def test_noalloc_matches_workspace_entry_point_twice():
+    check_twice([
+        # the larger problem first (its partials fill more of the buffer),
+        # then a smaller one that reuses the same buffer
+        (Workload("na1", 4, 32, 8, 1, 8192, 128, 128, False, torch.bfloat16, 4101), 0),
+        (Workload("na2", 1, 8, 2, 3, 1000, 64, 64, False, torch.bfloat16, 4102), 5),
+    ])
+
+
+def test_noalloc_wide_heads_twice():
+    # wide heads with V inside K (d_qk 576, d_v 512): 16 ranges of 256 rows
+    # take 8.4 MB of the 16 MiB buffer, then a smaller problem reuses it
+    check_twice([
+        (Workload("naw1", 1, 16, 1, 16, 2048, 576, 512, False, torch.bfloat16, 4103, v_from_k=True), 0),
+        (Workload("naw2", 1, 2, 1, 5, 300, 576, 512, False, torch.bfloat16, 4104, v_from_k=True), 3),
+    ])
