@@ -18,12 +18,14 @@
 //    blocks rb = 0, 1) computed whole (Sᵀ = K·Qᵀ, 18 k-steps of
 //    v_mfma_f32_16x16x32_bf16 each, both blocks' Q in registers), so every K
 //    fragment read feeds two MFMAs. They apply the mask and the exponential
-//    and write P (bf16) to LDS, and all four copy each K tile into LDS
-//    (LDS-DMA, a quarter each, one copy per two k-steps inside the score
-//    block), three tiles ahead, waiting for it at the end of the period.
+//    and write P (bf16) to LDS.
 //  * Value waves 4..7 (vw = w - 4) read the tile's P and accumulate output
 //    columns 128 vw .. 128 vw + 127 for all 64 rows (two 32-row blocks),
-//    their Vᵀ fragments read once from the K tile for both blocks.
+//    their Vᵀ fragments read once from the K tile for both blocks. At the
+//    start of each period they also copy a K tile into LDS (LDS-DMA, a
+//    quarter each), three tiles ahead, and wait for it at the period's end:
+//    an LDS-DMA holds its issuing wave for tens of cycles, and the value
+//    waves' path through a period is the shorter one.
 //  * Per tile the score waves' MFMAs for tile T + 1 and the value waves' for
 //    tile T share each SIMD's matrix pipe (36 16x16 + 16 32x32 MFMAs).
 //  * K tiles in a four-stage ring; P double-buffered; one barrier per tile.
@@ -55,9 +57,9 @@ struct WideVkSplitCfg {
     static constexpr int POFF = NSTAGE * KTILE_B;  // P buffers after the ring
     static constexpr int SOFF = POFF + 2 * PBUF_B; // row statistics: [2 key halves][64 rows] + m[64]
     static constexpr int LDS_BYTES = SOFF + 3 * TQ * 4;
-    static constexpr int KWIN_W = KTILE_B / 1024 / NSW;  // 1 KB copies per score wave per tile
+    static constexpr int KWIN_W = KTILE_B / 1024 / (NWAVE - NSW);  // 1 KB copies per value wave per tile
     static constexpr int CBW = DV / 32 / (NWAVE - NSW);  // 32-column blocks of O per value wave
-    static_assert(NKS == 18 && KWIN_W == 9, "the score block is written for 18 k-steps and 9 copies");
+    static_assert(NKS == 18 && KWIN_W == 9, "the score block is written for 18 k-steps; 9 copies per wave");
     static_assert(KCH % 8 == 0, "the swizzle permutes aligned groups of 8 chunks");
     static_assert(CBW == 4 && DV <= DQK, "value columns 128 vw .. 128 vw + 127");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
@@ -70,11 +72,9 @@ struct WideVkSplitCfg {
 // ks - 6 took the slot's old contents at issue, and waited for with a count of
 // this block's own ds_read_b128s (they complete in order). Each k-step runs
 // one MFMA per row block, s0 (rows 0..15 of the wave's 32) and s1 (16..31),
-// two independent chains. In the copying variant LDS-DMA u (1 KB, to LDS byte
-// address mb + 4096 u: pieces w, w + 4, ... of the tile) follows the MFMAs of
-// step 2 u, M0 written inside the statement, each DMA followed by a wait state. The block ends with the wait
-// states a VALU read of an MFMA result needs (the compiler does not see the
-// MFMA latency through the statement).
+// two independent chains. The block ends with the wait states a VALU read of
+// an MFMA result needs (the compiler does not see the MFMA latency through the
+// statement).
 #define WVKS_CLOBBERS "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255"
 #define WVKS_KR0 "ds_read_b128 v[232:235], %[kb0] offset:0\n\t"
 #define WVKS_KR1 "ds_read_b128 v[236:239], %[kb1] offset:0\n\t"
@@ -114,17 +114,6 @@ struct WideVkSplitCfg {
 #define WVKS_MM17 "s_waitcnt lgkmcnt(0)\n\tv_mfma_f32_16x16x32_bf16 %[s0], v[252:255], %[qa17], %[s0]\n\tv_mfma_f32_16x16x32_bf16 %[s1], v[252:255], %[qb17], %[s1]\n\t"
 #define WVKS_BODY WVKS_MM0 WVKS_KR6 WVKS_MM1 WVKS_KR7 WVKS_MM2 WVKS_KR8 WVKS_MM3 WVKS_KR9 WVKS_MM4 WVKS_KR10 WVKS_MM5 WVKS_KR11 WVKS_MM6 WVKS_KR12 WVKS_MM7 WVKS_KR13 WVKS_MM8 WVKS_KR14 WVKS_MM9 WVKS_KR15 WVKS_MM10 WVKS_KR16 WVKS_MM11 WVKS_KR17 WVKS_MM12 WVKS_MM13 WVKS_MM14 WVKS_MM15 WVKS_MM16 WVKS_MM17
 #define WVKS_Q_IN [qa0] "v"(qa[0]), [qa1] "v"(qa[1]), [qa2] "v"(qa[2]), [qa3] "v"(qa[3]), [qa4] "v"(qa[4]), [qa5] "v"(qa[5]), [qa6] "v"(qa[6]), [qa7] "v"(qa[7]), [qa8] "v"(qa[8]), [qa9] "v"(qa[9]), [qa10] "v"(qa[10]), [qa11] "v"(qa[11]), [qa12] "v"(qa[12]), [qa13] "v"(qa[13]), [qa14] "v"(qa[14]), [qa15] "v"(qa[15]), [qa16] "v"(qa[16]), [qa17] "v"(qa[17]), [qb0] "v"(qb[0]), [qb1] "v"(qb[1]), [qb2] "v"(qb[2]), [qb3] "v"(qb[3]), [qb4] "v"(qb[4]), [qb5] "v"(qb[5]), [qb6] "v"(qb[6]), [qb7] "v"(qb[7]), [qb8] "v"(qb[8]), [qb9] "v"(qb[9]), [qb10] "v"(qb[10]), [qb11] "v"(qb[11]), [qb12] "v"(qb[12]), [qb13] "v"(qb[13]), [qb14] "v"(qb[14]), [qb15] "v"(qb[15]), [qb16] "v"(qb[16]), [qb17] "v"(qb[17])
-#define WVKS_DMA4_0 "s_add_u32 m0, %[mb], 0\n\tbuffer_load_dwordx4 %[o0], %[rk], 0 offen lds\n\ts_nop 0\n\t"
-#define WVKS_DMA4_1 "s_add_u32 m0, %[mb], 4096\n\tbuffer_load_dwordx4 %[o1], %[rk], 0 offen lds\n\ts_nop 0\n\t"
-#define WVKS_DMA4_2 "s_add_u32 m0, %[mb], 8192\n\tbuffer_load_dwordx4 %[o2], %[rk], 0 offen lds\n\ts_nop 0\n\t"
-#define WVKS_DMA4_3 "s_add_u32 m0, %[mb], 12288\n\tbuffer_load_dwordx4 %[o3], %[rk], 0 offen lds\n\ts_nop 0\n\t"
-#define WVKS_DMA4_4 "s_add_u32 m0, %[mb], 16384\n\tbuffer_load_dwordx4 %[o4], %[rk], 0 offen lds\n\ts_nop 0\n\t"
-#define WVKS_DMA4_5 "s_add_u32 m0, %[mb], 20480\n\tbuffer_load_dwordx4 %[o5], %[rk], 0 offen lds\n\ts_nop 0\n\t"
-#define WVKS_DMA4_6 "s_add_u32 m0, %[mb], 24576\n\tbuffer_load_dwordx4 %[o6], %[rk], 0 offen lds\n\ts_nop 0\n\t"
-#define WVKS_DMA4_7 "s_add_u32 m0, %[mb], 28672\n\tbuffer_load_dwordx4 %[o7], %[rk], 0 offen lds\n\ts_nop 0\n\t"
-#define WVKS_DMA4_8 "s_add_u32 m0, %[mb], 32768\n\tbuffer_load_dwordx4 %[o8], %[rk], 0 offen lds\n\ts_nop 0\n\t"
-#define WVKS_BODY_COPY4 WVKS_MM0 WVKS_DMA4_0 WVKS_KR6 WVKS_MM1 WVKS_KR7 WVKS_MM2 WVKS_DMA4_1 WVKS_KR8 WVKS_MM3 WVKS_KR9 WVKS_MM4 WVKS_DMA4_2 WVKS_KR10 WVKS_MM5 WVKS_KR11 WVKS_MM6 WVKS_DMA4_3 WVKS_KR12 WVKS_MM7 WVKS_KR13 WVKS_MM8 WVKS_DMA4_4 WVKS_KR14 WVKS_MM9 WVKS_KR15 WVKS_MM10 WVKS_DMA4_5 WVKS_KR16 WVKS_MM11 WVKS_KR17 WVKS_MM12 WVKS_DMA4_6 WVKS_MM13 WVKS_MM14 WVKS_DMA4_7 WVKS_MM15 WVKS_MM16 WVKS_DMA4_8 WVKS_MM17
-#define WVKS_O9_IN [o0] "v"(o[0]), [o1] "v"(o[1]), [o2] "v"(o[2]), [o3] "v"(o[3]), [o4] "v"(o[4]), [o5] "v"(o[5]), [o6] "v"(o[6]), [o7] "v"(o[7]), [o8] "v"(o[8])
 
 
 __device__ __forceinline__ void wvks_kreads0(uint32_t kb0, uint32_t kb1) {
@@ -141,18 +130,6 @@ __device__ __forceinline__ void wvks_qk(const bf16x8 (&qa)[18], const bf16x8 (&q
                  : [s0] "=&v"(s0), [s1] "=&v"(s1)
                  : [kb0] "v"(kb0), [kb1] "v"(kb1), WVKS_Q_IN
                  : WVKS_CLOBBERS, "memory");
-    r0 = s0;
-    r1 = s1;
-}
-
-__device__ __forceinline__ void wvks_qk_copy(const bf16x8 (&qa)[18], const bf16x8 (&qb)[18], uint32_t kb0,
-                                             uint32_t kb1, const uint32_t (&o)[9], u32x4 rk, uint32_t mb,
-                                             f32x4 &r0, f32x4 &r1) {
-    f32x4 s0, s1;
-    asm volatile(WVKS_BODY_COPY4 "s_nop 7\n\ts_nop 7\n\ts_nop 3"
-                 : [s0] "=&v"(s0), [s1] "=&v"(s1)
-                 : [kb0] "v"(kb0), [kb1] "v"(kb1), WVKS_Q_IN, [mb] "s"(mb), [rk] "s"(rk), WVKS_O9_IN
-                 : WVKS_CLOBBERS, "memory", "scc");
     r0 = s0;
     r1 = s1;
 }
@@ -217,13 +194,14 @@ attn_fwd_wide_vk_split_kernel(const SplitArgs sa) {
     };
     float *stat = (float *)(lds + C::SOFF);  // [kh][64] per-half row values, then m[64]
 
-    // ---- K copies (score waves): in the period that computes the scores of
-    // range tile t + 1, every score wave w moves pieces 4 u + w (1 KB each) of
+    // ---- K copies (value waves): in the period that computes P·V of range
+    // tile t, value wave cw = w - 4 moves pieces 4 u + cw (1 KB each) of
     // range tile t + 3 and waits for them at the period's end.
+    const int cw = w & 3;
     auto copy_offsets = [&](uint32_t (&koff)[C::KWIN_W]) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < C::KWIN_W; ++u) {
-            const int p = (4 * u + w) * 64 + lane;
+            const int p = (4 * u + cw) * 64 + lane;
             const int r = p / C::KCH, c = wide_vk_chunk(r, p % C::KCH);
             koff[u] = (uint32_t)r * (uint32_t)a.k_sn * 2u + 16u * (uint32_t)c;
         }
@@ -244,7 +222,7 @@ attn_fwd_wide_vk_split_kernel(const SplitArgs sa) {
         unsigned char *st = lds + stage * C::KTILE_B;
         perturb_pause();
 #pragma unroll
-        for (int u = 0; u < C::KWIN_W; ++u) dma16_buf_to_lds(rk, koff[u], st + (4 * u + w) * 1024);
+        for (int u = 0; u < C::KWIN_W; ++u) dma16_buf_to_lds(rk, koff[u], st + (4 * u + cw) * 1024);
     };
     // the end of a period in which this wave copied: its copies have landed
     // (vmcnt(0): a partial count did not order the LDS-DMA writes), then the
@@ -252,10 +230,12 @@ attn_fwd_wide_vk_split_kernel(const SplitArgs sa) {
     auto copy_barrier = [&]() __attribute__((always_inline)) {
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     };
-    auto prologue = [&](const uint32_t(&koff)[C::KWIN_W], bool copies) __attribute__((always_inline)) {
+    // the first three tiles of the range (copied by the value waves, koff
+    // non-null), landed and published
+    auto prologue = [&](const uint32_t (*koff)[C::KWIN_W]) __attribute__((always_inline)) {
         __syncthreads();
-        if (copies)
-            for (int t = 0; t < 3 && t < n_tiles; ++t) dma_tile(koff, t, t);
+        if (koff)
+            for (int t = 0; t < 3 && t < n_tiles; ++t) dma_tile(*koff, t, t);
         asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     };
 
@@ -321,8 +301,6 @@ attn_fwd_wide_vk_split_kernel(const SplitArgs sa) {
             kb[0] = base + 64 * (0 ^ (sz >> 2));
             kb[1] = base + 64 * (1 ^ (sz >> 2));
         }
-        uint32_t koff[C::KWIN_W];
-        copy_offsets(koff);
         const int srow0 = q0 + 32 * rg + l16, srow1 = srow0 + 16;  // this lane's rows in the two blocks
         bf16x8 qa[C::NKS], qb[C::NKS];
         auto load_q = [&]() __attribute__((always_inline)) {
@@ -341,20 +319,11 @@ attn_fwd_wide_vk_split_kernel(const SplitArgs sa) {
             const uint32_t so = stage * C::KTILE_B;
             wvks_kreads0(kb[0] + so, kb[1] + so);
         };
-        // the score blocks of range tile t (first K reads issued); with tc >= 0
-        // this wave's share of the copy of range tile tc goes between the MFMAs
-        auto scores = [&](int t, int stage, float (&sv0)[4], float (&sv1)[4], int tc) __attribute__((always_inline)) {
+        // the score blocks of range tile t (first K reads issued)
+        auto scores = [&](int t, int stage, float (&sv0)[4], float (&sv1)[4]) __attribute__((always_inline)) {
             const uint32_t so = stage * C::KTILE_B;
             f32x4 s0, s1;
-            if (tc >= 0) {
-                const u32x4 rk = tile_rsrc(tc);
-                const uint32_t mb = __builtin_amdgcn_readfirstlane(
-                    lds_addr(lds + (tc & 3) * C::KTILE_B + w * 1024));
-                perturb_pause();
-                wvks_qk_copy(qa, qb, kb[0] + so, kb[1] + so, koff, rk, mb, s0, s1);
-            } else {
-                wvks_qk(qa, qb, kb[0] + so, kb[1] + so, s0, s1);
-            }
+            wvks_qk(qa, qb, kb[0] + so, kb[1] + so, s0, s1);
 #pragma unroll
             for (int i = 0; i < 4; ++i) sv0[i] = s0[i], sv1[i] = s1[i];
             const int key0 = (T0 + t) * TK + 16 * kh + 4 * G;
@@ -392,11 +361,11 @@ attn_fwd_wide_vk_split_kernel(const SplitArgs sa) {
         auto pass = [&](bool set_m) __attribute__((always_inline)) {
             l0 = 0.f, l1 = 0.f;
             load_q();
-            prologue(koff, true);
+            prologue(nullptr);
             kreads0(0);
             {
                 float sv0[4], sv1[4];
-                scores(0, 0, sv0, sv1, -1);
+                scores(0, 0, sv0, sv1);
                 if (set_m) {
                     float mx0, mx1;
                     combine_halves(block_row_max(sv0), block_row_max(sv1), true, mx0, mx1);
@@ -410,28 +379,24 @@ attn_fwd_wide_vk_split_kernel(const SplitArgs sa) {
             for (int t = 0; t + 1 < n_tiles; ++t) {
                 float sv0[4], sv1[4];
                 kreads0((t + 1) & 3);
-                const bool copies = t + 3 < n_tiles;
-                scores(t + 1, (t + 1) & 3, sv0, sv1, copies ? t + 3 : -1);
+                scores(t + 1, (t + 1) & 3, sv0, sv1);
                 block_p(t + 1, sv0, sv1);
-                copy_barrier();
+                lds_barrier();
             }
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no copy outlives the pass
         };
         auto max_pass = [&](float &M0, float &M1) __attribute__((always_inline)) {
             M0 = -INFINITY, M1 = -INFINITY;
             load_q();
-            prologue(koff, true);
+            prologue(nullptr);
             kreads0(0);
             for (int t = 0; t < n_tiles; ++t) {
                 float sv0[4], sv1[4];
-                scores(t, t & 3, sv0, sv1, -1);
+                scores(t, t & 3, sv0, sv1);
                 M0 = fmaxf(M0, block_row_max(sv0) * a.c);
                 M1 = fmaxf(M1, block_row_max(sv1) * a.c);
-                if (t + 3 < n_tiles) dma_tile(koff, t + 3, (t + 3) & 3);
-                copy_barrier();
+                lds_barrier();
                 if (t + 1 < n_tiles) kreads0((t + 1) & 3);
             }
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         };
         pass(true);
         float l_row[2], m_row[2];
@@ -449,7 +414,8 @@ attn_fwd_wide_vk_split_kernel(const SplitArgs sa) {
         }
     } else {
         // ================= value waves =================
-        const uint32_t koff[C::KWIN_W] = {};
+        uint32_t koff[C::KWIN_W];
+        copy_offsets(koff);
         uint32_t vtb[2][CBW];
         {
             const int i16 = lane & 15;
@@ -500,20 +466,26 @@ attn_fwd_wide_vk_split_kernel(const SplitArgs sa) {
                 for (int i = 0; i < CBW; ++i)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) oacc[rb][i][r] = 0.f;
-            prologue(koff, false);
+            prologue(&koff);
             if (set_m) {
                 float d0, d1;
                 combine_halves(0.f, 0.f, true, d0, d1);  // the score waves' reference barrier
             }
             lds_barrier();  // P(0) written
             for (int t = 0; t < n_tiles; ++t) {
+                if (t + 3 < n_tiles) dma_tile(koff, t + 3, (t + 3) & 3);
                 pv_tile(t);
-                if (t + 1 < n_tiles) lds_barrier();
+                if (t + 1 < n_tiles) copy_barrier();
             }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no copy outlives the pass
         };
         auto max_pass = [&]() __attribute__((always_inline)) {
-            prologue(koff, false);
-            for (int t = 0; t < n_tiles; ++t) lds_barrier();
+            prologue(&koff);
+            for (int t = 0; t < n_tiles; ++t) {
+                if (t + 3 < n_tiles) dma_tile(koff, t + 3, (t + 3) & 3);
+                copy_barrier();
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         };
         pass(true);
         float l_row[2], m_row[2];

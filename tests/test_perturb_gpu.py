@@ -137,6 +137,27 @@ def test_perturbed_split(libs, shape):
     oracle_check(o, lse, Oref, Lref)
 
 
+@pytest.mark.parametrize("shape", [(1, 3, 1, 130, 700, 3), (1, 2, 1, 40, 300, 0)],
+                         ids=["wide_ragged_3", "wide_library_count"])
+def test_perturbed_wide_split(libs, shape):
+    # the wide-head split kernel (V inside K): copies three tiles ahead in
+    # each range, ragged rows and a ragged last range
+    B, Hq, Hkv, Nq, Nkv, n = shape
+    w = Workload("ptws", B, Hq, Hkv, Nq, Nkv, 576, 512, False, torch.bfloat16, 78 + Nkv, v_from_k=True)
+    q, k, v = make_inputs(w, "cuda")
+    o, lse = check_perturbed(libs, "split", q, k, v, False, w.softmax_scale, n_splits=n)
+    Oref, Lref, _ = oracle.attention_fp64(q, k, v, False, w.softmax_scale)
+    oracle_check(o, lse, Oref, Lref)
+
+
+def test_perturbed_c5_split(libs):
+    q, k, v = make_inputs(C5, "cuda")
+    o, lse = check_perturbed(libs, "split", q, k, v, False, C5.softmax_scale)
+    rows = sample_rows(C5, 64)
+    Oref, Lref, _ = oracle.attention_fp64(q, k, v, False, C5.softmax_scale, rows=rows)
+    oracle_check(o, lse, Oref, Lref, rows=rows)
+
+
 @pytest.mark.parametrize("w", [C3, C4, C5], ids=["C3", "C4", "C5"])
 def test_perturbed_full_size(libs, w):
     # every element bit for bit against the normal build, sampled rows
