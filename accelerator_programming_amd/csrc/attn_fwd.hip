@@ -35,13 +35,16 @@ struct attn_fwd_plan {
     attn_fwd_params p;  // strides filled in
     int32_t variant;
     int32_t tile_q, tile_k, block, lds_bytes;
-    int64_t n_qtiles, grid;
+    int64_t n_qtiles, grid;   // grid: work items (query tiles x heads x batch)
+    int32_t persist_rounds;   // main kernel: 0, or items per workgroup of a kPersistGrid launch
     float c;  // scale * log2(e)
 };
 
 namespace {
 
 constexpr int64_t kMaxSlab = ((int64_t)1 << 31) - 1;
+// one main-kernel workgroup per CU of an MI355X (256 CUs in 8 XCDs)
+constexpr int64_t kPersistGrid = 256;
 
 bool fill_strides(int64_t s[3], int64_t H, int64_t N, int64_t d, int64_t row_min,
                   int64_t align_elems) {
@@ -107,13 +110,23 @@ attn_status validate(const attn_fwd_params *in, attn_fwd_plan *out) {
     out->n_qtiles = (p.N + out->tile_q - 1) / out->tile_q;
     out->grid = out->n_qtiles * p.B * p.H_q;
     if (out->grid > 0x7fffffff) return ATTN_ERR_UNSUPPORTED;
+    // the main kernel runs persistent workgroups, one per CU, when its items
+    // fill at least two whole rounds of them and its kv-head groups split
+    // evenly over the 8 XCDs (the work order keeps each group on one XCD)
+    out->persist_rounds = 0;
+    if (variant != V_D576_BF16 && (p.B * p.H_kv) % 8 == 0 && out->grid % kPersistGrid == 0 &&
+        out->grid >= 2 * kPersistGrid)
+        out->persist_rounds = (int32_t)(out->grid / kPersistGrid);
     out->c = (float)((double)p.scale * 1.4426950408889634074);
     return ATTN_OK;
 }
 
 template <int D, bool CAUSAL, typename T, bool DROP = false, bool ROPE = false>
-hipError_t launch(const attn_fwd_plan *pl, const KernelArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL((attn::attn_fwd_kernel<D, CAUSAL, T, DROP, ROPE>), dim3((uint32_t)pl->grid),
+hipError_t launch(const attn_fwd_plan *pl, const KernelArgs &a0, hipStream_t stream) {
+    KernelArgs a = a0;
+    a.persist_rounds = ROPE ? 0 : pl->persist_rounds;
+    const int64_t grid = a.persist_rounds > 0 ? kPersistGrid : pl->grid;
+    hipLaunchKernelGGL((attn::attn_fwd_kernel<D, CAUSAL, T, DROP, ROPE>), dim3((uint32_t)grid),
                        dim3(pl->block), 0, stream, a);
     return hipGetLastError();
 }
@@ -161,6 +174,7 @@ KernelArgs make_args(const attn_fwd_plan *plan, const void *Q, const void *K, co
                      float *lse) {
     const attn_fwd_params &p = plan->p;
     KernelArgs a;
+    a.persist_rounds = 0;
     a.q = Q;
     a.k = K;
     a.v = V;

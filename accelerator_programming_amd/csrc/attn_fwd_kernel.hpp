@@ -1,9 +1,11 @@
 // Fused attention forward kernel for gfx950.
 //
-// One workgroup owns one (batch, query head, tile of TQ = 256 query rows) and
-// writes that tile of O and logsumexp; no workgroup talks to another: the
-// disjoint-output-tile decomposition of "Distilling a 4.5 hour CUDA talk",
-// section 5. Inside it, the FlashAttention-2 structure of the same page's
+// One workgroup owns one (batch, query head, tile of TQ = 256 query rows) at a
+// time and writes that tile of O and logsumexp; no workgroup talks to
+// another: the disjoint-output-tile decomposition of "Distilling a 4.5 hour
+// CUDA talk", section 5. Where the items split evenly over the 256 CUs the
+// grid is one workgroup per CU, each taking its items in turn (no launch
+// between items on a CU). Inside it, the FlashAttention-2 structure of the same page's
 // section 7: the query tile stays in registers while K/V tiles stream through
 // on-chip memory (LDS), and the row softmax is carried across key tiles with
 // a per-row reference and a normalizer.
@@ -83,6 +85,9 @@ struct KernelArgs {
     float drop_scale;
     // RoPE of Q at load (kernels instantiated with ROPE only): log2(base)
     double rope_log2_base;
+    // main kernel: 0 (one work item per workgroup), or the number of items
+    // each workgroup takes in turn (gridDim.x a multiple of 8)
+    int32_t persist_rounds;
 };
 
 typedef short i16x2 __attribute__((ext_vector_type(2)));
@@ -164,10 +169,23 @@ attn_fwd_kernel(const KernelArgs a) {
     // evenly over them, each XCD takes whole groups and runs the query heads
     // of a group on the same q-tile side by side, so they read the same K/V
     // tiles through that XCD's L2. ------------------------------------------
+    // Persistent rounds: in round rnd the workgroups of an XCD take its next
+    // gridDim / 8 items, in reversed order every other round, so that heavy
+    // and light causal tiles pair up and every workgroup gets the same work.
+    // (Not with RoPE, whose Q load needs the registers the loop would keep.)
+    const int n_rounds = (!ROPE && a.persist_rounds > 0) ? a.persist_rounds : 1;
+    const uint32_t n_items = gridDim.x * (uint32_t)n_rounds;
+    for (int rnd = 0; rnd < n_rounds; ++rnd) {
     int b, h, qt;
     {
         const int n_groups = a.B * a.Hkv;
-        const int bid = work_index(blockIdx.x, gridDim.x);
+        uint32_t vbid = blockIdx.x;
+        if (n_rounds > 1) {
+            const uint32_t per_xcd = gridDim.x / 8, j = blockIdx.x / 8;
+            const uint32_t jj = (rnd & 1) ? per_xcd - 1 - j : j;
+            vbid = blockIdx.x % 8 + 8 * ((uint32_t)rnd * per_xcd + jj);
+        }
+        const int bid = work_index(vbid, n_items);
         if (n_groups % 8 == 0) {
             const int xcd = bid % 8, idx = bid / 8;
             const int per_round = (n_groups / 8) * a.group;  // WGs of one q-tile on one XCD
@@ -673,6 +691,9 @@ attn_fwd_kernel(const KernelArgs a) {
         if (g == 0 && a.lse)
             a.lse[((int64_t)b * a.Hq + h) * a.Nq + row] = (m + log2f(l_row)) * 0.69314718055994531f;
     }
+    // the next item's prologue copies overwrite the ring: every wave is past
+    // the fallback check's barrier, after its last read of this item's tiles
+    }  // work items
 #endif
 }
 

@@ -255,8 +255,11 @@ const char *attn_status_str(attn_status status);
 
 /*
  * attn_fwd_plan_info - launch geometry chosen by a plan, for tests and
- * reports: workgroups in the grid, threads per workgroup, query rows and key
- * rows per tile, and LDS bytes per workgroup. Any output pointer may be NULL.
+ * reports: work items (one per batch, query head and query tile; one
+ * workgroup each, or, where they fill whole rounds of the 256 CUs and the kv
+ * heads split evenly over the 8 XCDs, 256 persistent workgroups taking them
+ * in turn), threads per workgroup, query rows and key rows per tile, and LDS
+ * bytes per workgroup. Any output pointer may be NULL.
  */
 attn_status attn_fwd_plan_info(const attn_fwd_plan *plan, int64_t *grid, int32_t *block,
                                int32_t *tile_q, int32_t *tile_k, int32_t *lds_bytes);

@@ -457,6 +457,42 @@ def test_wide_split_needs_v_inside_k():
         op.close()
 
 
+# The main kernel runs one workgroup per CU taking its work items in turn
+# when the items fill whole rounds of 256 and the kv-head groups split evenly
+# over the 8 XCDs: these shapes give 512 items (two rounds, the second in
+# reversed order), with ragged last query tiles.
+PERSISTENT = [
+    # B, Hq, Hkv, N, d, causal
+    (8, 16, 1, 1000, 64, True),
+    (2, 32, 4, 2000, 128, True),
+    (1, 64, 8, 2048, 128, False),
+]
+
+
+@pytest.mark.parametrize("shape", PERSISTENT, ids=lambda s: "B%d_Hq%d_Hkv%d_N%d_d%d_%s" % (
+    s[0], s[1], s[2], s[3], s[4], "causal" if s[5] else "full"))
+def test_persistent_work_order(shape):
+    B, Hq, Hkv, N, d, causal = shape
+    w = Workload("persist", B, Hq, Hkv, N, N, d, d, causal, torch.bfloat16, 5150 + N + d)
+    plan = attn.attn_fwd_create(B, Hq, Hkv, N, d, causal, w.softmax_scale)
+    try:
+        assert attn.attn_fwd_plan_info(plan)["grid"] == 512
+    finally:
+        attn.attn_fwd_destroy(plan)
+    q, k, v = make_inputs(w, "cuda")
+    # every item is written exactly once: outputs start as NaN
+    o = torch.full((B, Hq, N, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((B, Hq, N), float("nan"), dtype=torch.float32, device="cuda")
+    op = attn.AttnFwd(q, k, v, causal, w.softmax_scale, o)
+    try:
+        op.run(q, k, v, o, lse)
+    finally:
+        op.close()
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    compare(o, lse, q, k, v, causal, w.softmax_scale, rows=sample_rows(w, 256))
+
+
 def test_binding_rejects_tensors_that_do_not_match_the_plan():
     # the kernels index memory from the plan: a smaller or differently laid
     # out tensor is refused in the binding, before any launch
