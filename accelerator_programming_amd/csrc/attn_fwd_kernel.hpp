@@ -642,7 +642,10 @@ attn_fwd_kernel(const KernelArgs a) {
         else
             pass(IC<1>{}, !exact);
         l_row = xhalf_sum(l);
-        if (exact) break;
+        if (exact) {
+            lds_barrier();  // every wave is done with the rings (the epilogue reuses them)
+            break;
+        }
         const bool bad = !(l_row <= kMaxL);  // also catches inf and NaN
         // the ballot runs in every lane (inside `lane == 0` it would see
         // lane 0's row only); lane 0 then publishes the wave's verdict
@@ -678,7 +681,37 @@ attn_fwd_kernel(const KernelArgs a) {
 
     // ---- O = Oᵀ / l (one reciprocal per row), logsumexp ---------------------
     const float inv_l = DROP ? a.drop_scale / l_row : 1.0f / l_row;
-    if (row < a.Nq) {
+    if constexpr (sizeof(TIn) == 2) {
+        // Through LDS (every wave is past its last read of the rings): each
+        // lane writes its row's 4-column runs to this wave's 32-row block,
+        // then each store covers whole rows (D / 8 lanes x 16 bytes a row)
+        // instead of 8 bytes in each of 32 rows. Staged rows are padded by 16
+        // bytes.
+        constexpr int SR = D + 8;
+        static_assert(C::NWAVE * C::ROWS * SR * 2 <= C::LDS_BYTES, "the staged O fits in the rings");
+        __bf16 *const stg = Kst + w * C::ROWS * SR;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int col = 32 * db + acc_row(4 * rr, g);
+                *(u32x2 *)(stg + l32 * SR + col) =
+                    u32x2{pack_bf16x2(oacc[db][4 * rr] * inv_l, oacc[db][4 * rr + 1] * inv_l),
+                          pack_bf16x2(oacc[db][4 * rr + 2] * inv_l, oacc[db][4 * rr + 3] * inv_l)};
+            }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        constexpr int LPR = D / 8, RPI = 64 / LPR;  // lanes per row, rows per store
+        const int rl = lane / LPR, cl = lane % LPR;
+#pragma unroll
+        for (int i = 0; i < C::ROWS / RPI; ++i) {
+            const int r = i * RPI + rl;
+            const u32x4 v = *(const u32x4 *)(stg + r * SR + 8 * cl);
+            if (wrow0 + r < a.Nq) *(u32x4 *)(Op + (int64_t)(wrow0 + r) * a.o_sn + 8 * cl) = v;
+        }
+        if (row < a.Nq && g == 0 && a.lse)
+            a.lse[((int64_t)b * a.Hq + h) * a.Nq + row] = (m + log2f(l_row)) * 0.69314718055994531f;
+        if (rnd + 1 < n_rounds) lds_barrier();  // the next item's first copies reuse the rings
+    } else if (row < a.Nq) {
         TIn *orow = Op + (int64_t)row * a.o_sn;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)

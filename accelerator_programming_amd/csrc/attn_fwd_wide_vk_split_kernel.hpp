@@ -366,6 +366,7 @@ attn_fwd_wide_vk_split_kernel(const SplitArgs sa) {
             {
                 float sv0[4], sv1[4];
                 scores(0, 0, sv0, sv1);
+                if (n_tiles > 1) kreads0(1);  // tile 1 landed in the prologue
                 if (set_m) {
                     float mx0, mx1;
                     combine_halves(block_row_max(sv0), block_row_max(sv1), true, mx0, mx1);
@@ -376,10 +377,13 @@ attn_fwd_wide_vk_split_kernel(const SplitArgs sa) {
                 block_p(0, sv0, sv1);
                 lds_barrier();  // P(0) written; tile 1 landed in the prologue
             }
+            // the first fragments of tile t + 2 are read right after the score
+            // block of tile t + 1 (that tile landed a period earlier, and the
+            // register ring is free), so the next block starts on them
             for (int t = 0; t + 1 < n_tiles; ++t) {
                 float sv0[4], sv1[4];
-                kreads0((t + 1) & 3);
                 scores(t + 1, (t + 1) & 3, sv0, sv1);
+                if (t + 2 < n_tiles) kreads0((t + 2) & 3);
                 block_p(t + 1, sv0, sv1);
                 lds_barrier();
             }
