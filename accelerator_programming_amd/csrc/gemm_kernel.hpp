@@ -27,7 +27,10 @@
 //  * Cᵀ blocks are computed, Cᵀ = B·Aᵀ, with v_mfma_f32_32x32x16_bf16: the A
 //    operand is a 32-row slab of B, the B operand a 32-row slab of A, both
 //    read from LDS as 16 contiguous bytes per lane. A lane then holds one row
-//    of C and runs of four consecutive columns, which it stores as 8 bytes.
+//    of C and runs of four consecutive columns. When C's rows allow 16-byte
+//    stores, each wave writes its 128 x 64 block into the idle LDS ring
+//    first and stores 8 rows of 128 contiguous bytes per instruction (16
+//    bytes in each of 32 rows otherwise).
 //  * K steps of 32: A and B slabs (256 x 32 bf16 = 16 KB each) go through a
 //    four-stage LDS ring (128 KB) by LDS-DMA (buffer_load ... lds). Two copy
 //    groups (waves 0-3, waves 4-7) alternate: in step t the group t mod 2
@@ -55,6 +58,7 @@ struct GemmArgs {
     int32_t M, N, K;
     int32_t lda, ldb, ldc;  // row strides in elements
     int32_t tiles_m, tiles_n;
+    int32_t stage_c;  // C rows 16-byte aligned (ldc % 8 == 0, C % 16 == 0): stores go through LDS
 };
 
 struct GemmCfg {
@@ -65,7 +69,12 @@ struct GemmCfg {
     static constexpr int NSTAGE = 4;
     static constexpr int SLAB = BM * BK;           // elements of one A (or B) slab
     static constexpr int STAGE_BYTES = 2 * SLAB * 2;
-    static constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES;  // 128 KB
+    static constexpr int RING_BYTES = NSTAGE * STAGE_BYTES;  // 128 KB
+    // the epilogue stages each wave's 128 x 64 block of C in LDS, rows padded
+    // to 144 bytes (the ring is idle by then)
+    static constexpr int CROW_B = 2 * 64 + 16;
+    static constexpr int STAGE_C_BYTES = NWAVE * 128 * CROW_B;
+    static constexpr int LDS_BYTES = RING_BYTES > STAGE_C_BYTES ? RING_BYTES : STAGE_C_BYTES;
     // LDS-DMA windows of 64 lanes x 16 B = 16 rows of 64 B; a slab is 16
     // windows, so one step's A and B slabs are 32 windows, 16 per wave of the
     // copying group
@@ -258,7 +267,44 @@ gemm_bf16_nt_kernel(const GemmArgs a) {
         k_loop(GIC<1>{});
     wait_copies();  // no copy outlives the workgroup
 
-    // ---- epilogue: C row m0 + 128wm + 32mb + l32, columns in runs of four ----
+    // ---- epilogue -------------------------------------------------------------
+    if (a.stage_c) {
+        // Through LDS, once every wave's copies have landed (the barrier):
+        // each lane writes its row's runs of four columns to this wave's
+        // 128-row block, then each store covers 8 rows of 128 contiguous bytes
+        // instead of 16 bytes in each of 32 rows.
+        barrier();
+        static_assert(C::WM == 128 && C::WN == 64, "the staged block is 128 x 64");
+        unsigned char *const stg = lds_raw + w * 128 * C::CROW_B;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < NB; ++i)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int col = 32 * i + acc_row(4 * rr, g);
+                    *(u32x2 *)(stg + (32 * j + l32) * C::CROW_B + 2 * col) =
+                        u32x2{pack_bf16x2(acc[i][j][4 * rr], acc[i][j][4 * rr + 1]),
+                              pack_bf16x2(acc[i][j][4 * rr + 2], acc[i][j][4 * rr + 3])};
+                }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const int rl = lane >> 3, cl = lane & 7;  // 8 lanes x 16 bytes per row
+        const int col = n0 + C::WN * wn + 8 * cl;
+#pragma unroll
+        for (int it = 0; it < 16; ++it) {
+            const int r = 8 * it + rl;
+            const u32x4 v = *(const u32x4 *)(stg + r * C::CROW_B + 16 * cl);
+            const int row = m0 + C::WM * wm + r;
+            if (row < a.M && col < a.N) {
+                __bf16 *p = a.c + (int64_t)row * a.ldc + col;
+                if (col + 8 <= a.N)
+                    *(u32x4 *)p = v;
+                else
+                    *(u32x2 *)p = u32x2{v[0], v[1]};  // N is a multiple of 4
+            }
+        }
+    } else {
+    // C row m0 + 128wm + 32mb + l32, columns in runs of four
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int row = m0 + C::WM * wm + 32 * j + l32;
@@ -273,6 +319,7 @@ gemm_bf16_nt_kernel(const GemmArgs a) {
                     store4(crow + col, acc[i][j][4 * rr], acc[i][j][4 * rr + 1],
                            acc[i][j][4 * rr + 2], acc[i][j][4 * rr + 3]);
             }
+    }
     }
 #endif
 }

@@ -39,6 +39,8 @@ extern "C" attn_status tile_gemm_bf16_nt(int64_t M, int64_t N, int64_t K, const 
     a.ldc = (int32_t)ldc;
     a.tiles_m = (int32_t)tiles_m;
     a.tiles_n = (int32_t)tiles_n;
+    // 16-byte C rows: the epilogue stores whole row pieces through LDS
+    a.stage_c = (ldc % 8 == 0 && ((uintptr_t)C & 15) == 0) ? 1 : 0;
     hipLaunchKernelGGL(attn::gemm_bf16_nt_kernel, dim3((uint32_t)(tiles_m * tiles_n)), dim3(G::NT), 0,
                        (hipStream_t)stream, a);
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;

@@ -83,6 +83,19 @@ def test_strided_operands_and_output():
     assert (out_big[:, N:] == 7.0).all()
 
 
+def test_output_rows_staged_with_a_partial_last_chunk():
+    # ldc a multiple of 8 (the epilogue goes through LDS) and N = 268: the
+    # last 16-byte piece of each row holds 4 columns of C and 4 past N
+    M, N, K = 300, 268, 96
+    a = randn_bf16(M, K, seed=13)
+    b = randn_bf16(N, K, seed=14)
+    out_big = torch.full((M, 280), 7.0, dtype=torch.bfloat16, device="cuda")
+    out = out_big[:, :N]
+    gemm.gemm_nt(a, b, out=out)
+    check(out, a, b)
+    assert (out_big[:, N:] == 7.0).all()
+
+
 def test_k_zero_writes_zeros():
     out = torch.full((64, 32), 3.0, dtype=torch.bfloat16, device="cuda")
     # zero-width operands have no storage: hand the C ABI aligned stand-ins of
