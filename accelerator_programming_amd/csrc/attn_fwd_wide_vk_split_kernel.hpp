@@ -504,22 +504,38 @@ attn_fwd_wide_vk_split_kernel(const SplitArgs sa) {
         }
 
         // ---- this range's O / l (fp32) and logsumexp, per row -----------------
+        // Through LDS (every wave is past the statistics' barriers and every
+        // copy has landed; the staged blocks end below the P buffers and the
+        // statistics): each lane writes its rows' runs of four columns to this
+        // wave's 64-row block (rows padded by 16 bytes), then each store
+        // covers two rows' 512 contiguous bytes instead of 16 bytes in each of
+        // 32 rows.
+        constexpr int SRB = 4 * 32 * CBW + 16;
+        static_assert((C::NWAVE - C::NSW) * C::TQ * SRB <= C::POFF, "the staged O stays in the K ring");
+        unsigned char *const stg = lds + vw * C::TQ * SRB;
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
-            const int row = q0 + 32 * rb + l32;
-            if (row >= a.Nq) continue;
             const float inv_l = 1.0f / l_row[rb];
-            float *orow = opart + (prow0 + row) * DV;
 #pragma unroll
             for (int i = 0; i < CBW; ++i)
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
-                    const int col = 32 * (CBW * vw + i) + acc_row(4 * rr, g);
-                    *(f32x4 *)(orow + col) = f32x4{oacc[rb][i][4 * rr] * inv_l, oacc[rb][i][4 * rr + 1] * inv_l,
-                                                   oacc[rb][i][4 * rr + 2] * inv_l, oacc[rb][i][4 * rr + 3] * inv_l};
+                    const int col = 32 * i + acc_row(4 * rr, g);
+                    *(f32x4 *)(stg + (32 * rb + l32) * SRB + 4 * col) =
+                        f32x4{oacc[rb][i][4 * rr] * inv_l, oacc[rb][i][4 * rr + 1] * inv_l,
+                              oacc[rb][i][4 * rr + 2] * inv_l, oacc[rb][i][4 * rr + 3] * inv_l};
                 }
-            if (vw == 0 && g == 0)
+            const int row = q0 + 32 * rb + l32;
+            if (vw == 0 && g == 0 && row < a.Nq)
                 lpart[prow0 + row] = (m_row[rb] + log2f(l_row[rb])) * 0.69314718055994531f;
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const int rl = lane >> 5, cl = lane & 31;  // 32 lanes x 16 bytes per row
+#pragma unroll
+        for (int it = 0; it < C::TQ / 2; ++it) {
+            const int r = 2 * it + rl;
+            const f32x4 v = *(const f32x4 *)(stg + r * SRB + 16 * cl);
+            if (q0 + r < a.Nq) *(f32x4 *)(opart + (prow0 + q0 + r) * DV + 32 * CBW * vw + 4 * cl) = v;
         }
     }
 #endif
