@@ -579,20 +579,34 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
         }
 
         // ---- O = Oᵀ / l (one reciprocal per row), logsumexp -----------------
+        // Through LDS (every copy has landed and every wave is past the
+        // statistics' barriers; the staged blocks end below the P buffers):
+        // each lane writes its row's runs of four columns to this wave's
+        // block (rows padded by 16 bytes), then each store covers four rows'
+        // 256 contiguous bytes instead of 8 bytes in each of 32 rows.
         const float inv_l = 1.0f / l_row;
-        if (row < a.Nq) {
-            __bf16 *orow = Op + (int64_t)row * a.o_sn;
+        constexpr int SRB = 2 * 32 * CBW + 16;
+        static_assert((C::NWAVE - C::NSW) * C::TQ * SRB <= C::POFF, "the staged O stays in the K ring");
+        unsigned char *const stg = lds + vw * C::TQ * SRB;
 #pragma unroll
-            for (int i = 0; i < CBW; ++i)
+        for (int i = 0; i < CBW; ++i)
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int col = 32 * (CBW * vw + i) + acc_row(4 * rr, g);
-                    store4(orow + col, oacc[i][4 * rr] * inv_l, oacc[i][4 * rr + 1] * inv_l,
-                           oacc[i][4 * rr + 2] * inv_l, oacc[i][4 * rr + 3] * inv_l);
-                }
-            if (vw == 0 && g == 0 && a.lse)
-                a.lse[((int64_t)b * a.Hq + h) * a.Nq + row] = (m_row + log2f(l_row)) * 0.69314718055994531f;
+            for (int rr = 0; rr < 4; ++rr) {
+                const int col = 32 * i + acc_row(4 * rr, g);
+                *(u32x2 *)(stg + l32 * SRB + 2 * col) =
+                    u32x2{pack_bf16x2(oacc[i][4 * rr] * inv_l, oacc[i][4 * rr + 1] * inv_l),
+                          pack_bf16x2(oacc[i][4 * rr + 2] * inv_l, oacc[i][4 * rr + 3] * inv_l)};
+            }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const int rl = lane >> 4, cl = lane & 15;  // 16 lanes x 16 bytes per row
+#pragma unroll
+        for (int it = 0; it < C::TQ / 4; ++it) {
+            const int r = 4 * it + rl;
+            const u32x4 v = *(const u32x4 *)(stg + r * SRB + 16 * cl);
+            if (q0 + r < a.Nq) *(u32x4 *)(Op + (int64_t)(q0 + r) * a.o_sn + 32 * CBW * vw + 8 * cl) = v;
         }
+        if (row < a.Nq && vw == 0 && g == 0 && a.lse)
+            a.lse[((int64_t)b * a.Hq + h) * a.Nq + row] = (m_row + log2f(l_row)) * 0.69314718055994531f;
     }
 #endif
 }
