@@ -63,6 +63,25 @@ def test_dropout_parity(case):
     check(o, lse, q, k, v, causal, w.softmax_scale, int(p * 256), seed)
 
 
+def test_dropout_with_persistent_workgroups():
+    # 512 work items over 8 kv-head groups: the main kernel runs 256
+    # persistent workgroups taking two items each; the keep decisions depend
+    # only on (seed, b, h, i, j), so the order items are taken in must not
+    # show; sampled rows against the oracle, every row written (NaN start)
+    w = Workload("drop_persist", 8, 16, 1, 1000, 1000, 64, 64, True, torch.bfloat16, 4343)
+    q, k, v = make_inputs(w, "cuda")
+    o = torch.full((8, 16, 1000, 64), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((8, 16, 1000), float("nan"), dtype=torch.float32, device="cuda")
+    op = attn.AttnFwd(q, k, v, True, w.softmax_scale, o)
+    try:
+        op.run_dropout(q, k, v, o, lse, p_drop=0.25, seed=99)
+    finally:
+        op.close()
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    check(o, lse, q, k, v, True, w.softmax_scale, 64, 99, rows=sample_rows(w, 192))
+
+
 def _random_drop(n: int, seed: int):
     import random
     rng = random.Random(seed)

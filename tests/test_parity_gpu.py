@@ -462,29 +462,27 @@ def test_wide_split_needs_v_inside_k():
 # over the 8 XCDs: these shapes give 512 items (two rounds, the second in
 # reversed order), with ragged last query tiles.
 PERSISTENT = [
-    # B, Hq, Hkv, N, d, causal
-    (8, 16, 1, 1000, 64, True),
-    (2, 32, 4, 2000, 128, True),
-    (1, 64, 8, 2048, 128, False),
+    # B, Hq, Hkv, N, d, causal, fp32
+    (8, 16, 1, 1000, 64, True, False),
+    (2, 32, 4, 2000, 128, True, False),
+    (1, 64, 8, 2048, 128, False, False),
+    (8, 16, 1, 1000, 64, True, True),    # fp32 inputs (their own epilogue)
 ]
 
 
-@pytest.mark.parametrize("shape", PERSISTENT, ids=lambda s: "B%d_Hq%d_Hkv%d_N%d_d%d_%s" % (
-    s[0], s[1], s[2], s[3], s[4], "causal" if s[5] else "full"))
+@pytest.mark.parametrize("shape", PERSISTENT, ids=lambda s: "B%d_Hq%d_Hkv%d_N%d_d%d_%s%s" % (
+    s[0], s[1], s[2], s[3], s[4], "causal" if s[5] else "full", "_fp32" if s[6] else ""))
 def test_persistent_work_order(shape):
-    B, Hq, Hkv, N, d, causal = shape
-    w = Workload("persist", B, Hq, Hkv, N, N, d, d, causal, torch.bfloat16, 5150 + N + d)
-    plan = attn.attn_fwd_create(B, Hq, Hkv, N, d, causal, w.softmax_scale)
-    try:
-        assert attn.attn_fwd_plan_info(plan)["grid"] == 512
-    finally:
-        attn.attn_fwd_destroy(plan)
+    B, Hq, Hkv, N, d, causal, fp32 = shape
+    dtype = torch.float32 if fp32 else torch.bfloat16
+    w = Workload("persist", B, Hq, Hkv, N, N, d, d, causal, dtype, 5150 + N + d)
     q, k, v = make_inputs(w, "cuda")
     # every item is written exactly once: outputs start as NaN
-    o = torch.full((B, Hq, N, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    o = torch.full((B, Hq, N, d), float("nan"), dtype=dtype, device="cuda")
     lse = torch.full((B, Hq, N), float("nan"), dtype=torch.float32, device="cuda")
     op = attn.AttnFwd(q, k, v, causal, w.softmax_scale, o)
     try:
+        assert attn.attn_fwd_plan_info(op.plan)["grid"] == 512
         op.run(q, k, v, o, lse)
     finally:
         op.close()
