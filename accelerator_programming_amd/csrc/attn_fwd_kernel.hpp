@@ -685,27 +685,37 @@ attn_fwd_kernel(const KernelArgs a) {
         // Through LDS (every wave is past its last read of the rings): each
         // lane writes its row's 4-column runs to this wave's 32-row block,
         // then each store covers whole rows (D / 8 lanes x 16 bytes a row)
-        // instead of 8 bytes in each of 32 rows. Staged rows are padded by 16
-        // bytes.
-        constexpr int SR = D + 8;
-        static_assert(C::NWAVE * C::ROWS * SR * 2 <= C::LDS_BYTES, "the staged O fits in the rings");
-        __bf16 *const stg = Kst + w * C::ROWS * SR;
+        // instead of 8 bytes in each of 32 rows. Rows are unpadded; the
+        // 16-byte chunk of a run is XORed with row bits (1..3 at D = 64, 0..3
+        // at D = 128) and its 8-byte half with row bit 4, so the 32 lanes of
+        // a write pass reach every bank once and a row's chunks stay a
+        // permutation for the reads.
+        constexpr int CPRS = D / 8;                        // 16-byte chunks per row
+        auto swz = [](int r) { return D >= 128 ? (r & 15) : ((r >> 1) & 7); };
+        static_assert(C::NWAVE * C::ROWS * D * 2 <= C::LDS_BYTES, "the staged O fits in the rings");
+        __bf16 *const stg = Kst + w * C::ROWS * D;
+        // opaque copies of the lane index: the staging addresses are formed
+        // here, not hoisted out of the item loop to stay live through it
+        int el = lane;
+        asm volatile("" : "+v"(el));
+        const int el32 = el & 31, eg = el >> 5;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
-                const int col = 32 * db + acc_row(4 * rr, g);
-                *(u32x2 *)(stg + l32 * SR + col) =
+                const int ch = (4 * db + rr) ^ swz(el32), hf = eg ^ ((el32 >> 4) & 1);
+                *(u32x2 *)(stg + el32 * D + 8 * ch + 4 * hf) =
                     u32x2{pack_bf16x2(oacc[db][4 * rr] * inv_l, oacc[db][4 * rr + 1] * inv_l),
                           pack_bf16x2(oacc[db][4 * rr + 2] * inv_l, oacc[db][4 * rr + 3] * inv_l)};
             }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        constexpr int LPR = D / 8, RPI = 64 / LPR;  // lanes per row, rows per store
-        const int rl = lane / LPR, cl = lane % LPR;
+        constexpr int RPI = 64 / CPRS;  // rows per store
+        const int rl = el / CPRS, cl = el % CPRS;
 #pragma unroll
         for (int i = 0; i < C::ROWS / RPI; ++i) {
             const int r = i * RPI + rl;
-            const u32x4 v = *(const u32x4 *)(stg + r * SR + 8 * cl);
+            u32x4 v = *(const u32x4 *)(stg + r * D + 8 * (cl ^ swz(r)));
+            if ((r >> 4) & 1) v = u32x4{v[2], v[3], v[0], v[1]};
             if (wrow0 + r < a.Nq) *(u32x4 *)(Op + (int64_t)(wrow0 + r) * a.o_sn + 8 * cl) = v;
         }
         if (row < a.Nq && g == 0 && a.lse)

@@ -70,9 +70,9 @@ struct GemmCfg {
     static constexpr int SLAB = BM * BK;           // elements of one A (or B) slab
     static constexpr int STAGE_BYTES = 2 * SLAB * 2;
     static constexpr int RING_BYTES = NSTAGE * STAGE_BYTES;  // 128 KB
-    // the epilogue stages each wave's 128 x 64 block of C in LDS, rows padded
-    // to 144 bytes (the ring is idle by then)
-    static constexpr int CROW_B = 2 * 64 + 16;
+    // the epilogue stages each wave's 128 x 64 block of C in LDS (the ring is
+    // idle by then), 128-byte rows
+    static constexpr int CROW_B = 2 * 64;
     static constexpr int STAGE_C_BYTES = NWAVE * 128 * CROW_B;
     static constexpr int LDS_BYTES = RING_BYTES > STAGE_C_BYTES ? RING_BYTES : STAGE_C_BYTES;
     // LDS-DMA windows of 64 lanes x 16 B = 16 rows of 64 B; a slab is 16
@@ -275,6 +275,10 @@ gemm_bf16_nt_kernel(const GemmArgs a) {
         // instead of 16 bytes in each of 32 rows.
         barrier();
         static_assert(C::WM == 128 && C::WN == 64, "the staged block is 128 x 64");
+        // the 16-byte chunk of a run is XORed with row bits 1..3 and its
+        // 8-byte half with row bit 4: the 32 lanes of a write pass reach
+        // every bank once, and a row's chunks stay a permutation for the reads
+        auto swz = [](int r) { return (r >> 1) & 7; };
         unsigned char *const stg = lds_raw + w * 128 * C::CROW_B;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -282,8 +286,9 @@ gemm_bf16_nt_kernel(const GemmArgs a) {
             for (int i = 0; i < NB; ++i)
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
-                    const int col = 32 * i + acc_row(4 * rr, g);
-                    *(u32x2 *)(stg + (32 * j + l32) * C::CROW_B + 2 * col) =
+                    const int r = 32 * j + l32;
+                    const int ch = (4 * i + rr) ^ swz(r), hf = g ^ ((r >> 4) & 1);
+                    *(u32x2 *)(stg + r * C::CROW_B + 16 * ch + 8 * hf) =
                         u32x2{pack_bf16x2(acc[i][j][4 * rr], acc[i][j][4 * rr + 1]),
                               pack_bf16x2(acc[i][j][4 * rr + 2], acc[i][j][4 * rr + 3])};
                 }
@@ -293,7 +298,8 @@ gemm_bf16_nt_kernel(const GemmArgs a) {
 #pragma unroll
         for (int it = 0; it < 16; ++it) {
             const int r = 8 * it + rl;
-            const u32x4 v = *(const u32x4 *)(stg + r * C::CROW_B + 16 * cl);
+            u32x4 v = *(const u32x4 *)(stg + r * C::CROW_B + 16 * (cl ^ swz(r)));
+            if ((r >> 4) & 1) v = u32x4{v[2], v[3], v[0], v[1]};
             const int row = m0 + C::WM * wm + r;
             if (row < a.M && col < a.N) {
                 __bf16 *p = a.c + (int64_t)row * a.ldc + col;
