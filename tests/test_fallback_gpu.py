@@ -249,3 +249,31 @@ def test_wide_split_path_with_outlier_keys():
     o, lse = run(q, k, v, False, w.softmax_scale, "split", n_splits=2)
     Oref, Lref, _ = oracle.attention_fp64(q, k, v, False, w.softmax_scale)
     compare(o, lse, Oref, Lref)
+
+
+def test_fallback_inside_persistent_workgroups():
+    # 512 work items over 8 kv-head groups: 256 persistent workgroups take two
+    # items each; some items go through the exact pass and others do not, and
+    # each is followed by another item on the same workgroup
+    w = Workload("fbp", 8, 16, 1, 1000, 1000, 64, 64, True, torch.bfloat16, 918)
+    plants = [(0, 3, 700, 300, 32.0, "over"), (5, 9, 260, 100, 32.0, "over"),
+              (7, 15, 999, 998, 32.0, "over"), (2, 0, 130, 90, 8.0, "mid")]
+    q, k, v = make(w, plants)
+    o = torch.full((8, 16, 1000, 64), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((8, 16, 1000), float("nan"), dtype=torch.float32, device="cuda")
+    op = attn.AttnFwd(q, k, v, True, w.softmax_scale, o)
+    try:
+        assert attn.attn_fwd_plan_info(op.plan)["grid"] == 512
+        op.run(q, k, v, o, lse)
+    finally:
+        op.close()
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    # the planted rows and their neighbours, plus a spread of the rest
+    rows = [(b, h, i) for b, h, i, _, _, _ in plants] + [(b, h, min(i + 1, 999)) for b, h, i, _, _, _ in plants]
+    rng = np.random.default_rng(918)
+    rows += [(int(rng.integers(8)), int(rng.integers(16)), int(rng.integers(1000))) for _ in range(120)]
+    rows = np.array(rows)
+    Oref, Lref, _ = oracle.attention_fp64(q, k, v, True, w.softmax_scale, rows=rows)
+    r = torch.as_tensor(rows)
+    compare(o[r[:, 0], r[:, 1], r[:, 2]], lse[r[:, 0], r[:, 1], r[:, 2]], Oref, Lref)
