@@ -582,18 +582,21 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
         // Through LDS (every copy has landed and every wave is past the
         // statistics' barriers; the staged blocks end below the P buffers):
         // each lane writes its row's runs of four columns to this wave's
-        // block (rows padded by 16 bytes), then each store covers four rows'
-        // 256 contiguous bytes instead of 8 bytes in each of 32 rows.
+        // block, then each store covers four rows' 256 contiguous bytes
+        // instead of 8 bytes in each of 32 rows. Rows are unpadded: a run's
+        // 16-byte chunk is XORed with row bits 0..3 and its 8-byte half with
+        // row bit 4, so the 32 lanes of a write pass reach every bank once.
         const float inv_l = 1.0f / l_row;
-        constexpr int SRB = 2 * 32 * CBW + 16;
+        constexpr int SRB = 2 * 32 * CBW;
         static_assert((C::NWAVE - C::NSW) * C::TQ * SRB <= C::POFF, "the staged O stays in the K ring");
+        static_assert(SRB == 256, "16 chunks a row");
         unsigned char *const stg = lds + vw * C::TQ * SRB;
 #pragma unroll
         for (int i = 0; i < CBW; ++i)
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
-                const int col = 32 * i + acc_row(4 * rr, g);
-                *(u32x2 *)(stg + l32 * SRB + 2 * col) =
+                const int ch = (4 * i + rr) ^ (l32 & 15), hf = g ^ ((l32 >> 4) & 1);
+                *(u32x2 *)(stg + l32 * SRB + 16 * ch + 8 * hf) =
                     u32x2{pack_bf16x2(oacc[i][4 * rr] * inv_l, oacc[i][4 * rr + 1] * inv_l),
                           pack_bf16x2(oacc[i][4 * rr + 2] * inv_l, oacc[i][4 * rr + 3] * inv_l)};
             }
@@ -602,7 +605,8 @@ attn_fwd_wide_vk_kernel(const KernelArgs a) {
 #pragma unroll
         for (int it = 0; it < C::TQ / 4; ++it) {
             const int r = 4 * it + rl;
-            const u32x4 v = *(const u32x4 *)(stg + r * SRB + 16 * cl);
+            u32x4 v = *(const u32x4 *)(stg + r * SRB + 16 * (cl ^ (r & 15)));
+            if ((r >> 4) & 1) v = u32x4{v[2], v[3], v[0], v[1]};
             if (q0 + r < a.Nq) *(u32x4 *)(Op + (int64_t)(q0 + r) * a.o_sn + 32 * CBW * vw + 8 * cl) = v;
         }
         if (row < a.Nq && vw == 0 && g == 0 && a.lse)
